@@ -1,0 +1,26 @@
+"""Ragged paged attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``librpa.so`` (hand-written HIP kernels behind the C ABI declared in
+``include/rpa.h``); this package only marshals PyTorch tensors into that ABI.  There is no
+CPU fallback: every call fails loudly if the library or a gfx950 device is missing.
+
+    write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, ...)
+    attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, ...)
+    build_union_tables(mask, base_tables, past, kv_len, page_size)
+"""
+from ._rpa import (  # noqa: F401
+    KERNEL_AUTO,
+    KERNEL_DECODE,
+    KERNEL_MIXED,
+    KERNEL_PREFILL,
+    LAYOUT_HEAD_MAJOR,
+    LAYOUT_SEQ_MAJOR,
+    RpaError,
+    attention,
+    build_union_tables,
+    library_path,
+    load_library,
+    select_kernel,
+    workspace_size,
+    write_kv,
+)

@@ -1,0 +1,228 @@
+"""ctypes binding of librpa.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module turns PyTorch
+tensors into the raw pointers, sizes and host mirrors the C ABI (include/rpa.h) takes,
+passes torch's current HIP stream, and raises on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LAYOUT_SEQ_MAJOR = 0
+LAYOUT_HEAD_MAJOR = 1
+KERNEL_AUTO = 0
+KERNEL_DECODE = 1
+KERNEL_PREFILL = 2
+KERNEL_MIXED = 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librpa.so")
+
+_STATUS = {0: "RPA_OK", 1: "RPA_ERR_INVALID_ARGUMENT", 2: "RPA_ERR_UNSUPPORTED",
+           3: "RPA_ERR_WORKSPACE_TOO_SMALL", 4: "RPA_ERR_HIP"}
+
+EXPORTED = ("rpa_write_kv", "rpa_attention_workspace_size", "rpa_select_kernel", "rpa_attention",
+            "rpa_build_union_tables", "rpa_last_error")
+
+
+class RpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class RpaShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("h_cu_q_lens", ctypes.POINTER(ctypes.c_int32)),
+        ("h_kv_lens", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load librpa.so (built in-tree by attention_ragged_paged_amd.build); no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m attention_ragged_paged_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    shp = ctypes.POINTER(RpaShape)
+    lib.rpa_write_kv.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.rpa_write_kv.restype = ctypes.c_int
+    lib.rpa_attention_workspace_size.argtypes = [shp]
+    lib.rpa_attention_workspace_size.restype = sz
+    lib.rpa_select_kernel.argtypes = [shp]
+    lib.rpa_select_kernel.restype = i32
+    lib.rpa_attention.argtypes = [shp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.rpa_attention.restype = ctypes.c_int
+    lib.rpa_build_union_tables.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.rpa_build_union_tables.restype = ctypes.c_int
+    lib.rpa_last_error.argtypes = []
+    lib.rpa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RpaError(status, load_library().rpa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _host_i32(t):
+    h = t.detach().to("cpu", torch.int32).contiguous()
+    return h, h.data_ptr()
+
+
+def _need_contig(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+class _Shape:
+    """An RpaShape plus the host tensors it points into (kept alive with it)."""
+
+    def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                 max_pages, layout, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+        self.cu, cu_p = _host_i32(cu_q_lens_host)
+        self.kv, kv_p = _host_i32(kv_lens_host)
+        B = self.cu.numel() - 1
+        self.c = RpaShape(B, int(self.cu[-1]) if B >= 0 else 0, num_q_heads, num_kv_heads, head_dim,
+                          page_size, num_pages, max_pages, layout, kernel,
+                          ctypes.cast(cu_p, ctypes.POINTER(ctypes.c_int32)),
+                          ctypes.cast(kv_p, ctypes.POINTER(ctypes.c_int32)))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _cache_geometry(k_cache, block_tables):
+    if k_cache.dim() == 4:   # [P, S, Hkv, D]
+        return LAYOUT_SEQ_MAJOR, k_cache.shape[2], k_cache.shape[1], k_cache.shape[3]
+    if k_cache.dim() == 3:   # [P, S, D], tables [B, Hkv, max_pages]
+        return LAYOUT_HEAD_MAJOR, block_tables.shape[1], k_cache.shape[1], k_cache.shape[2]
+    raise ValueError("k_cache must be [P, S, Hkv, D] (sequence-major) or [P, S, D] (KV-head-major)")
+
+
+def _shape_for(q_heads, k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host, kv_lens_host,
+               kernel):
+    layout, Hkv, S, D = _cache_geometry(k_cache, block_tables)
+    return _Shape(num_q_heads=q_heads, num_kv_heads=Hkv, head_dim=D, page_size=S,
+                  num_pages=k_cache.shape[0], max_pages=block_tables.shape[-1], layout=layout,
+                  cu_q_lens_host=cu_q_lens if cu_q_lens_host is None else cu_q_lens_host,
+                  kv_lens_host=kv_lens if kv_lens_host is None else kv_lens_host, kernel=kernel)
+
+
+def write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *,
+             cu_q_lens_host=None, kv_lens_host=None):
+    """Scatter k_new / v_new ([T, Hkv, D] bf16) into the paged caches in place (rpa_write_kv)."""
+    lib = load_library()
+    _need_contig(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                 block_tables=block_tables, cu_q_lens=cu_q_lens, kv_lens=kv_lens)
+    shape = _shape_for(k_new.shape[1] if k_new.dim() == 3 else 1, k_cache, block_tables, cu_q_lens,
+                       kv_lens, cu_q_lens_host, kv_lens_host, KERNEL_AUTO)
+    _check(lib.rpa_write_kv(shape.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                            _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens),
+                            _stream(k_cache.device)))
+
+
+def workspace_size(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+    lib = load_library()
+    shape = _shape_for(q.shape[1], k_cache, block_tables, None, None, cu_q_lens_host, kv_lens_host,
+                       kernel)
+    n = lib.rpa_attention_workspace_size(shape.ref)
+    if n == ctypes.c_size_t(-1).value:
+        _check(1)
+    return int(n)
+
+
+def select_kernel(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+    lib = load_library()
+    shape = _shape_for(q.shape[1], k_cache, block_tables, None, None, cu_q_lens_host, kv_lens_host,
+                       kernel)
+    k = lib.rpa_select_kernel(shape.ref)
+    if k < 0:
+        _check(1)
+    return int(k)
+
+
+def attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *, k_new=None,
+              v_new=None, out=None, workspace=None, cu_q_lens_host=None, kv_lens_host=None,
+              kernel=KERNEL_AUTO):
+    """Ragged paged causal GQA attention (rpa_attention); returns out [T, Hq, D] bf16.
+
+    cu_q_lens_host / kv_lens_host: CPU int32 mirrors of the device metadata; when omitted
+    they are copied from the device (a synchronising copy).
+    """
+    lib = load_library()
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
+    shape = _shape_for(q.shape[1], k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host,
+                       kv_lens_host, kernel)
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib.rpa_attention_workspace_size(shape.ref)
+    if need == ctypes.c_size_t(-1).value:
+        _check(1)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.rpa_attention(shape.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                             _ptr(cu_q_lens), _ptr(kv_lens), float(scale), _ptr(k_new),
+                             _ptr(v_new), _ptr(out), _ptr(workspace), ws_bytes,
+                             _stream(q.device)))
+    return out
+
+
+def build_union_tables(mask, base_tables, past, kv_len, page_size, *, out_tables=None,
+                       out_counts=None, out_kv_lens=None):
+    """Per-KV-head block tables of one chunk (rpa_build_union_tables).
+
+    mask: uint8 [Hq, nQB, nKB] (device); base_tables: int32 [Hkv, nKB] (device).
+    Returns (tables [Hkv, nKB], counts [Hkv], kv_lens [Hkv]), all int32 on the device.
+    """
+    lib = load_library()
+    _need_contig(mask=mask, base_tables=base_tables)
+    Hq, nQB, nKB = mask.shape
+    Hkv = base_tables.shape[0]
+    dev = mask.device
+    if out_tables is None:
+        out_tables = torch.empty((Hkv, nKB), dtype=torch.int32, device=dev)
+    if out_counts is None:
+        out_counts = torch.empty(Hkv, dtype=torch.int32, device=dev)
+    if out_kv_lens is None:
+        out_kv_lens = torch.empty(Hkv, dtype=torch.int32, device=dev)
+    _check(lib.rpa_build_union_tables(_ptr(mask), Hq, Hkv, nQB, nKB, _ptr(base_tables), int(past),
+                                      int(kv_len), int(page_size), _ptr(out_tables),
+                                      _ptr(out_counts), _ptr(out_kv_lens), _stream(dev)))
+    return out_tables, out_counts, out_kv_lens

@@ -1,0 +1,636 @@
+// Ragged paged causal GQA attention for gfx950: decode, prefill and mixed kernels.
+//
+// Method: "Ragged Paged Attention: A High-Performance and Flexible LLM Inference Kernel for
+// TPU" (summary card, "Key ideas"): attention over ragged batches whose K/V live in a paged
+// cache, with separate kernels for decode, prefill and mixed batches.  Kernel split and
+// split-K decode follow ONNX Runtime PR 31727 ("[WebGPU] Optimized PagedAttention
+// implementation (2/n)", "What's shipped": a split-reduce decode pair and a fused paged
+// prefill with page-table-aware tile loads); causal alignment is that page's seqlens_q
+// fix: token t of a sequence sits at position past + t and sees keys 0 .. past + t.
+//
+// Work decomposition.  Every kernel maps blockIdx onto a work item with an in-kernel scan
+// over the sequences (find_item), so no work list is built or uploaded per call:
+//   decode item  = (sequence, KV head, 16-row tile, KV split)   one 256-thread workgroup
+//   prefill item = (sequence, 128-row tile, KV head, KV split)  one 256-thread workgroup
+// A row is one (token, query head) pair; the query heads of a GQA group are packed into the
+// same item so every K/V byte is read once per group.  Items whose sequence has more than
+// one split write fp32 partials (running max, sum, unnormalised output) that the merge
+// kernel combines with the log-sum-exp rule; single-split items write bf16 output directly.
+//
+// MFMA layouts (gfx950, wave64).  Scores are computed transposed, S^T = K Q^T, so that a
+// lane owns one query row: its softmax statistics need at most two cross-lane steps, and
+// the S^T accumulator is already the B operand of the P V product computed as
+// O^T = V^T P^T.  V^T comes out of LDS with the transposing read ds_read_b64_tr_b16.
+#include "rpa_device.h"
+#include "rpa_launch.h"
+
+namespace rpa {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int seq_of_token_dev(const int32_t *cu_q_lens, int B, int token) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q_lens[mid] <= token)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int64_t kv_row_offset(const AttnArgs &a, int page, int slot, int g) {
+  return (int64_t)page * a.page_stride + (int64_t)slot * a.slot_stride + (int64_t)g * a.head_stride;
+}
+
+__device__ __forceinline__ int table_at(const AttnArgs &a, int b, int g, int logical) {
+  return a.tables[b * a.bt_seq_stride + g * a.bt_head_stride + logical];
+}
+
+// ============================================================================ decode ======
+//
+// A decode item holds up to 16 query rows (the q_len * G rows of one KV head, 16 at a time)
+// and one KV split.  The 4 waves of the workgroup take 16-key chunks round-robin; each wave
+// keeps its own online-softmax state, and the 4 states are merged through LDS at the end.
+//   QK^T: v_mfma_f32_16x16x32_bf16, A = K chunk (16 keys x 32 dims, straight from global
+//         memory: a lane's 16-byte load is exactly its operand), B = Q^T (in registers).
+//         Lane l gets S^T[key 4(l/16) + i][row l%16], i = 0..3.
+//   PV:   v_mfma_f32_16x16x16_bf16, A = V^T (transposing LDS read of the staged chunk),
+//         B = P^T (the lane's own 4 probabilities), accumulating O^T[dim][row].
+template <int D>
+struct DecodeSmem {
+  union {
+    uint16_t v[4][16 * D];   // per-wave staged V chunk, swizzled rows
+    float o[4][16][D + 4];   // per-wave unnormalised outputs for the final combine
+  };
+  float m[4][16];
+  float l[4][16];
+};
+
+template <int D>
+__device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
+  const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
+  if (q_len == 0 || !is_decode_class(a, q_len)) return 0;
+  return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits(a, b, q_len);
+}
+
+template <int D>
+__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
+  constexpr int KK = D / 32;  // 16x16x32 MFMAs per 16-key chunk for QK^T (and loads per lane)
+  constexpr int MB = D / 16;  // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
+  DecodeSmem<D> &sm = *reinterpret_cast<DecodeSmem<D> *>(smem_raw);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
+  const int r16 = lane & 15;
+  const int j = lane >> 4;
+
+  const ItemRef it = find_item(id, a.B, [&](int b) { return decode_count<D>(a, b); });
+  const int b = __builtin_amdgcn_readfirstlane(it.b);
+  if (b < 0) return;
+  const int q0 = a.cu_q_lens[b];
+  const int q_len = a.cu_q_lens[b + 1] - q0;
+  const int n_rt = ceil_div(q_len * a.G, kDecodeRows);
+  const int nsplit = num_splits(a, b, q_len);
+  int rem = __builtin_amdgcn_readfirstlane(it.rem);
+  const int s = rem % nsplit;
+  rem /= nsplit;
+  const int rt = rem % n_rt;
+  const int g = rem / n_rt;
+  const int kv_len = kv_len_of(a, b, g);
+  const int past = kv_len - q_len;
+  const int n_rows = q_len * a.G;
+  const int last_row = min(rt * kDecodeRows + kDecodeRows - 1, n_rows - 1);
+  const int k_begin = s * a.split_dec;
+  const int k_end = min(min(kv_len, k_begin + a.split_dec), past + last_row / a.G + 1);
+
+  // This lane's query row (B operand column l%16).
+  const int fr = rt * kDecodeRows + r16;
+  const bool row_ok = fr < n_rows;
+  const int t_row = row_ok ? fr / a.G : 0;
+  const int h_row = g * a.G + (row_ok ? fr % a.G : 0);
+  const int row_lim = past + t_row + 1;  // keys < row_lim are visible to this row
+  bf16x8 qf[KK];
+  {
+    const uint16_t *qp = a.q + ((int64_t)(q0 + t_row) * a.Hq + h_row) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * j);
+      qf[kk] = as_bf16x8(v);
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_all = k_end > k_begin ? ceil_div(k_end - k_begin, 16) : 0;
+  const int n_w = n_all > w ? (n_all - w + 3) / 4 : 0;  // chunks w, w+4, ... of this wave
+  uint16_t *vbuf = sm.v[w];
+  const int page_mask = (1 << a.page_shift) - 1;
+
+  // Pages of this wave's chunks, 64 chunks per window: lane l holds the page of chunk
+  // base + l, so the pipelined loop picks pages with a register read, never a memory load.
+  int pg_lane = 0;
+  auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
+    const int key0 = k_begin + 16 * (w + 4 * (base + i));
+    const int page = __builtin_amdgcn_readlane(pg_lane, i);
+    const int64_t off = kv_row_offset(a, page, (key0 & page_mask) + r16, g);
+    const uint16_t *kp = a.k_cache + off + 8 * j;
+    const uint16_t *vp = a.v_cache + off + 8 * j;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kr[kk] = *reinterpret_cast<const u32x4 *>(kp + 32 * kk);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) vr[kk] = *reinterpret_cast<const u32x4 *>(vp + 32 * kk);
+  };
+
+  auto process_chunk = [&](int i, const u32x4 *kr, const u32x4 *vr) {
+    const int key0 = k_begin + 16 * (w + 4 * i);
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) st = mfma16x16x32(as_bf16x8(kr[kk]), qf[kk], st);
+    // Stage V (rows of keys past the item's range are zeroed: they may hold anything).
+    const bool vrow_ok = key0 + r16 < k_end;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = vrow_ok ? vr[kk] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r16, 4 * kk + j)) = v;
+    }
+    float sv[4];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int key = key0 + 4 * j + i4;
+      const bool ok = key < k_end && key < row_lim;
+      sv[i4] = ok ? st[i4] * a.scale_log2 : kNegInf;
+      mloc = fmaxf(mloc, sv[i4]);
+    }
+    mloc = wave_max_xor(mloc, 16);
+    mloc = wave_max_xor(mloc, 32);
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      p[i4] = fast_exp2(sv[i4] - m_use);
+      psum += p[i4];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const uint32_t p01 = pack_bf16x2(p[0], p[1]);
+    const uint32_t p23 = pack_bf16x2(p[2], p[3]);
+    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+    // Transposing read: lane (i = l%16, j) names row 4j + i/4, dims 16mb + 4(i%4) .. +3.
+    const int tr_row = 4 * j + (r16 >> 2);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int c = 2 * mb + ((r16 & 3) >> 1);
+      const s16x4 va = lds_read_tr(vbuf + lds_off<D>(tr_row, c) + 4 * (r16 & 1));
+      acc[mb] = acc[mb] * alpha;
+      acc[mb] = mfma16x16x16(va, pb, acc[mb]);
+    }
+  };
+
+  for (int base = 0; base < n_w; base += 64) {
+    const int n = min(64, n_w - base);
+    {
+      const int i = base + lane;
+      pg_lane = lane < n ? table_at(a, b, g, (k_begin + 16 * (w + 4 * i)) >> a.page_shift) : 0;
+    }
+    u32x4 kA[KK], vA[KK], kB[KK], vB[KK];
+    load_chunk(base, 0, kA, vA);
+    // Two chunks per trip, register double buffer.  Every load is unconditional (the last
+    // one may repeat the final chunk, an L2 hit) so that the wait before each chunk's use
+    // covers exactly that chunk's loads while the other chunk's loads stay in flight.
+    for (int i = 0; i + 1 < n; i += 2) {
+      load_chunk(base, i + 1, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this chunk's math
+      process_chunk(base + i, kA, vA);
+      load_chunk(base, min(i + 2, n - 1), kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      process_chunk(base + i + 1, kB, vB);
+    }
+    if (n & 1) process_chunk(base + n - 1, kA, vA);
+  }
+
+  // Row sum over the 4 lanes that share the row.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  __syncthreads();  // every wave is done with its V buffer (aliased by the combine area)
+  if (j == 0) {
+    sm.m[w][r16] = m_run;
+    sm.l[w][r16] = l_run;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) sm.o[w][r16][16 * mb + 4 * j + i4] = acc[mb][i4];
+  __syncthreads();
+
+  // Combine the 4 waves: thread -> (row, D/16 consecutive dims).
+  constexpr int DPT = D / 16;
+  const int row = threadIdx.x >> 4;
+  const int d0 = (threadIdx.x & 15) * DPT;
+  float M = kNegInf;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm.m[ww][row]);
+  const float M_use = M == kNegInf ? 0.f : M;
+  float wgt[4];
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    wgt[ww] = fast_exp2(sm.m[ww][row] - M_use);
+    L += sm.l[ww][row] * wgt[ww];
+  }
+  float o[DPT];
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) x += sm.o[ww][row][d0 + d] * wgt[ww];
+    o[d] = x;
+  }
+  const int frow = rt * kDecodeRows + row;
+  if (frow >= n_rows) return;
+  const int token = q0 + frow / a.G;
+  const int h = g * a.G + frow % a.G;
+  if (nsplit == 1) {
+    const float inv = 1.f / L;
+    uint32_t packed[DPT / 2];
+#pragma unroll
+    for (int d = 0; d < DPT / 2; ++d) packed[d] = pack_bf16x2(o[2 * d] * inv, o[2 * d + 1] * inv);
+    uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
+    if constexpr (DPT == 8)
+      *reinterpret_cast<u32x4 *>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    else
+      *reinterpret_cast<u32x2 *>(op) = u32x2{packed[0], packed[1]};
+  } else {
+    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h;
+    float *po = a.part_o + prow * D + d0;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4)
+      *reinterpret_cast<f32x4 *>(po + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]};
+    if (d0 == 0) {
+      a.part_ml[prow * 2 + 0] = M;
+      a.part_ml[prow * 2 + 1] = L;
+    }
+  }
+}
+
+// =========================================================================== prefill ======
+//
+// A prefill item is 128 query rows of one KV head: pf_tokens = 128 / G consecutive tokens of
+// each of the G query heads of the group (wave w owns rows 32w .. 32w+31).  The workgroup
+// walks 64-key tiles up to the causal limit of its last token.  Each tile is fetched into
+// registers one tile ahead, so the global loads of tile i+1 overlap the MFMAs of tile i;
+// block-table entries sit in a register (one per lane) and never delay a tile load.  Every key row is located through the block table
+// on its own, so a 64-key tile may span several pages (page size 16 or 32 included).
+//   QK^T: v_mfma_f32_32x32x16_bf16, A = K tile rows from LDS (ds_read_b128), B = Q^T in
+//         registers.  Lane l gets S^T[key 32mb + 8(v/4) + 4(l/32) + v%4][row l%32].
+//   PV:   v_mfma_f32_32x32x16_bf16, A = V^T from two transposing LDS reads, B = P^T taken
+//         from the lane's own S^T registers (k-slot e of lane half h maps to key
+//         16kb + 8(e/4) + 4h + e%4, and the V^T reads use the same order).
+template <int D>
+struct PrefillSmem {
+  uint16_t k[kPrefillKeys * D];
+  uint16_t v[kPrefillKeys * D];
+};
+
+template <int D>
+__device__ __forceinline__ int prefill_count(const AttnArgs &a, int b) {
+  const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
+  if (q_len == 0 || is_decode_class(a, q_len)) return 0;
+  return a.Hkv * ceil_div(q_len, a.pf_tokens) * num_splits(a, b, q_len);
+}
+
+template <int D>
+__device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
+  constexpr int KS = D / 16;                               // QK^T MFMAs per 32-key block
+  constexpr int MD = D / 32;                               // PV output blocks of 32 dims
+  constexpr int LOADS = kPrefillKeys * (D / 8) / kThreads;  // 16-byte loads per thread per tile
+  constexpr int kChunks = D / 8;
+  PrefillSmem<D> &sm = *reinterpret_cast<PrefillSmem<D> *>(smem_raw);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int r32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const ItemRef it = find_item(id, a.B, [&](int b) { return prefill_count<D>(a, b); });
+  const int b = __builtin_amdgcn_readfirstlane(it.b);
+  if (b < 0) return;
+  const int q0 = a.cu_q_lens[b];
+  const int q_len = a.cu_q_lens[b + 1] - q0;
+  const int n_qt = ceil_div(q_len, a.pf_tokens);
+  const int nsplit = num_splits(a, b, q_len);
+  int rem = __builtin_amdgcn_readfirstlane(it.rem);
+  const int s = rem % nsplit;
+  rem /= nsplit;
+  const int g = rem % a.Hkv;
+  const int qt = n_qt - 1 - rem / a.Hkv;  // heaviest (latest) query tiles first
+  const int kv_len = kv_len_of(a, b, g);
+  const int past = kv_len - q_len;
+  const int t_first = qt * a.pf_tokens;
+  const int t_last = min(q_len - 1, t_first + a.pf_tokens - 1);
+  const int k_begin = s * a.split_pf;
+  const int k_end = min(min(kv_len, k_begin + a.split_pf), past + t_last + 1);
+  const int n_tiles = k_end > k_begin ? ceil_div(k_end - k_begin, kPrefillKeys) : 0;
+
+  // This lane's query row.
+  const int rr = 32 * w + r32;
+  const int hg = rr / a.pf_tokens;
+  const int t_row = t_first + rr % a.pf_tokens;
+  const bool row_ok = hg < a.G && t_row < q_len;
+  const int h_row = g * a.G + (row_ok ? hg : 0);
+  const int row_lim = past + (row_ok ? t_row : 0) + 1;
+  bf16x8 qf[KS];
+  {
+    const uint16_t *qp = a.q + ((int64_t)(q0 + (row_ok ? t_row : 0)) * a.Hq + h_row) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * hf);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 acc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[md][v] = 0.f;
+
+  const int page_mask = (1 << a.page_shift) - 1;
+  // Pages of the item's logical blocks, 64 at a time: lane l holds block pg_blk0 + l.  A tile
+  // spans at most 4 blocks, so a reload happens only when a tile runs past the window.
+  const int blk_begin = k_begin >> a.page_shift;
+  const int blk_end = k_end > 0 ? ((k_end - 1) >> a.page_shift) + 1 : 0;
+  int pg_lane = 0, pg_blk0 = 0;
+  auto fetch_pages = [&](int blk0) {
+    const int blk = blk0 + lane;
+    pg_lane = blk < blk_end ? table_at(a, b, g, blk) : 0;
+    pg_blk0 = blk0;
+  };
+  // Per-thread tile rows: load u covers chunk (u*256 + tid) of the 64 x D tile.
+  u32x4 kr[LOADS], vr[LOADS];
+  auto fetch_tile = [&](int tile) {
+    const int kt0 = k_begin + tile * kPrefillKeys;
+    const int last_blk = (min(kt0 + kPrefillKeys, k_end) - 1) >> a.page_shift;
+    if (last_blk - pg_blk0 >= 64) fetch_pages(kt0 >> a.page_shift);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = u * kThreads + tid;
+      const int pos = min(kt0 + cid / kChunks, k_end - 1);
+      const int page = __shfl(pg_lane, (pos >> a.page_shift) - pg_blk0);
+      const int64_t off = kv_row_offset(a, page, pos & page_mask, g) + (cid % kChunks) * 8;
+      kr[u] = *reinterpret_cast<const u32x4 *>(a.k_cache + off);
+      vr[u] = *reinterpret_cast<const u32x4 *>(a.v_cache + off);
+    }
+  };
+
+  if (n_tiles > 0) {
+    fetch_pages(blk_begin);
+    fetch_tile(0);
+  }
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int kt0 = k_begin + tile * kPrefillKeys;
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = u * kThreads + tid;
+      const int key = cid / kChunks;
+      const int c = cid % kChunks;
+      *reinterpret_cast<u32x4 *>(&sm.k[lds_off<D>(key, c)]) = kr[u];
+      const bool ok = kt0 + key < k_end;
+      *reinterpret_cast<u32x4 *>(&sm.v[lds_off<D>(key, c)]) = ok ? vr[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    if (tile + 1 < n_tiles) fetch_tile(tile + 1);
+
+    // S^T = K Q^T for the 64-key tile: two 32-key blocks.
+    f32x16 st[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[mb][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(&sm.k[lds_off<D>(32 * mb + r32, 2 * ks + hf)]);
+        st[mb] = mfma32x32x16(as_bf16x8(kv), qf[ks], st[mb]);
+      }
+    }
+    // Scale, mask (only tiles that reach past some row's limit or the range end), max.
+    const bool need_mask = kt0 + kPrefillKeys > k_end || kt0 + kPrefillKeys - 1 > past + t_first;
+    float mloc = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = st[mb][v] * a.scale_log2;
+        if (need_mask) {
+          const int key = kt0 + 32 * mb + 8 * (v >> 2) + 4 * hf + (v & 3);
+          x = (key < k_end && key < row_lim) ? x : kNegInf;
+        }
+        st[mb][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = wave_max_xor(mloc, 32);
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int mb = kb >> 1;
+      const int v0 = 8 * (kb & 1);
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = fast_exp2(st[mb][v0 + e] - m_use);
+        const float p1 = fast_exp2(st[mb][v0 + e + 1] - m_use);
+        psum += p0 + p1;
+        w4[e >> 1] = pack_bf16x2(p0, p1);
+      }
+      pb[kb] = as_bf16x8(u32x4{w4[0], w4[1], w4[2], w4[3]});
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = acc[md] * alpha;
+
+    // O^T += V^T P^T.  Lane (i = l%16, quarter q = l/16): half h = q/2 picks keys
+    // 16kb + 4h + (0..3) and + 8; q%2 picks the 16-dim half of the 32-dim block.
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int tr_key = 4 * (q4 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int c = 4 * md + 2 * (q4 & 1) + ((i16 & 3) >> 1);
+      const int eo = 4 * (i16 & 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = 16 * kb + tr_key;
+        const s16x4 lo = lds_read_tr(&sm.v[lds_off<D>(key, c) + eo]);
+        const s16x4 hi = lds_read_tr(&sm.v[lds_off<D>(key + 8, c) + eo]);
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+        acc[md] = mfma32x32x16(va, pb[kb], acc[md]);
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const int token = q0 + t_row;
+  if (nsplit == 1) {
+    const float inv = 1.f / l_run;
+    uint16_t *op = a.out + ((int64_t)token * a.Hq + h_row) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int d = 32 * md + 8 * vq + 4 * hf;
+        const uint32_t w0 = pack_bf16x2(acc[md][4 * vq + 0] * inv, acc[md][4 * vq + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(acc[md][4 * vq + 2] * inv, acc[md][4 * vq + 3] * inv);
+        *reinterpret_cast<u32x2 *>(op + d) = u32x2{w0, w1};
+      }
+  } else {
+    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h_row;
+    float *po = a.part_o + prow * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int d = 32 * md + 8 * vq + 4 * hf;
+        *reinterpret_cast<f32x4 *>(po + d) =
+            f32x4{acc[md][4 * vq], acc[md][4 * vq + 1], acc[md][4 * vq + 2], acc[md][4 * vq + 3]};
+      }
+    if (hf == 0) {
+      a.part_ml[prow * 2 + 0] = m_run;
+      a.part_ml[prow * 2 + 1] = l_run;
+    }
+  }
+}
+
+// =========================================================================== kernels ======
+
+template <int D>
+constexpr size_t kSmemBytes =
+    sizeof(DecodeSmem<D>) > sizeof(PrefillSmem<D>) ? sizeof(DecodeSmem<D>) : sizeof(PrefillSmem<D>);
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
+  decode_item<D>(a, blockIdx.x, smem);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(PrefillSmem<D>)];
+  prefill_item<D>(a, blockIdx.x, smem);
+}
+
+// One launch for a batch holding both kinds: prefill items first (they are the longest),
+// then decode items.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D>];
+  if ((int)blockIdx.x < a.n_pf_items)
+    prefill_item<D>(a, blockIdx.x, smem);
+  else
+    decode_item<D>(a, blockIdx.x - a.n_pf_items, smem);
+}
+
+// Split-K merge (the reduce half of the split-reduce decode pair): one wave per
+// (token, query head) row whose sequence was split.  out = sum_s o_s 2^(m_s - M) /
+// sum_s l_s 2^(m_s - M), M = max_s m_s.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = lane_id();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.T * a.Hq) return;
+  const int token = row / a.Hq;
+  const int h = row % a.Hq;
+  const int b = seq_of_token_dev(a.cu_q_lens, a.B, token);
+  const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
+  const int nsplit = num_splits(a, b, q_len);
+  if (nsplit <= 1) return;
+  float m_s = kNegInf, l_s = 0.f;
+  if (lane < nsplit) {
+    const int64_t prow = ((int64_t)lane * a.T + token) * a.Hq + h;
+    m_s = a.part_ml[prow * 2 + 0];
+    l_s = a.part_ml[prow * 2 + 1];
+  }
+  float M = m_s;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float M_use = M == kNegInf ? 0.f : M;
+  const float wgt = fast_exp2(m_s - M_use);
+  float L = l_s * wgt;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+  float o[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) o[d] = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float ws = __shfl(wgt, sp);
+    if (ws == 0.f) continue;
+    const float *po = a.part_o + (((int64_t)sp * a.T + token) * a.Hq + h) * D + lane * DPL;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) o[d] += po[d] * ws;
+  }
+  const float inv = 1.f / L;
+  uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + lane * DPL;
+  if constexpr (DPL == 2) {
+    *reinterpret_cast<uint32_t *>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  } else {
+    const uint32_t pk = pack_bf16x2(o[0] * inv, 0.f);
+    op[0] = (uint16_t)(pk & 0xffffu);
+  }
+}
+
+template <int D>
+static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_items, bool merge,
+                                     hipStream_t stream) {
+  if (n_items > 0) {
+    const dim3 grid((unsigned)n_items), block(kThreads);
+    switch (kind) {
+      case AttnKernel::kDecode:
+        hipLaunchKernelGGL(decode_kernel<D>, grid, block, 0, stream, a);
+        break;
+      case AttnKernel::kPrefill:
+        hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, a);
+        break;
+      case AttnKernel::kMixed:
+        hipLaunchKernelGGL(mixed_kernel<D>, grid, block, 0, stream, a);
+        break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (merge) {
+    const unsigned rows = (unsigned)((int64_t)a.T * a.Hq);
+    hipLaunchKernelGGL(merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_items, bool merge,
+                            hipStream_t stream) {
+  if (D == 128) return launch_attention_d<128>(a, kind, n_items, merge, stream);
+  return launch_attention_d<64>(a, kind, n_items, merge, stream);
+}
+
+}  // namespace rpa

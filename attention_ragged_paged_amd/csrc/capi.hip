@@ -1,0 +1,417 @@
+// C ABI of librpa: validation, batch classification, dispatch and launches.
+//
+// Conventions follow ONNX Runtime PR 31727 ("[WebGPU] Optimized PagedAttention
+// implementation (2/n)"): specific error messages per check, token_count == 0 returns OK
+// without a launch, caches updated in place, block sizes are powers of two >= 16, and the
+// kernel is chosen by a pure function of the batch shape ("distribution-aware" dispatch of
+// the Ragged Paged Attention card, "Key ideas": separate decode, prefill and mixed kernels).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/rpa.h"
+#include "rpa_device.h"
+#include "rpa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rpa_status fail(rpa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rpa_status ok() {
+  g_last_error.clear();
+  return RPA_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+int cdiv(long long x, long long y) { return (int)((x + y - 1) / y); }
+
+// Decode-class threshold in query rows (q_len * G): one 16-row MFMA tile.
+constexpr int kDecodeRowsMax = 16;
+// Largest number of KV splits of one sequence (one merge wave holds one split per lane).
+constexpr int kMaxSplits = 64;
+// Work items the split sizes aim for: several workgroups per compute unit of the
+// 256-CU chip so the tail of a ragged batch stays short.
+constexpr long long kTargetItems = 2048;
+
+int kv_len_at(const rpa_shape *s, int b, int g) {
+  return s->layout == RPA_LAYOUT_SEQ_MAJOR ? s->h_kv_lens[b]
+                                           : s->h_kv_lens[(long long)b * s->num_kv_heads + g];
+}
+
+int max_kv_len_host(const rpa_shape *s, int b) {
+  int m = kv_len_at(s, b, 0);
+  if (s->layout == RPA_LAYOUT_HEAD_MAJOR)
+    for (int g = 1; g < s->num_kv_heads; ++g) m = std::max(m, kv_len_at(s, b, g));
+  return m;
+}
+
+rpa_status validate(const rpa_shape *s, bool need_lens) {
+  if (!s) return fail(RPA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->num_seqs < 0) return fail(RPA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", s->num_seqs);
+  if (s->total_q < 0) return fail(RPA_ERR_INVALID_ARGUMENT, "total_q %d < 0", s->total_q);
+  if (s->num_kv_heads <= 0 || s->num_q_heads <= 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "num_q_heads %d and num_kv_heads %d must be > 0",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->head_dim <= 0 || s->head_dim % 8 != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "head_dim %d must be a positive multiple of 8",
+                s->head_dim);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RPA_ERR_UNSUPPORTED, "head_dim %d is not built (64 and 128 are)", s->head_dim);
+  if (s->num_q_heads / s->num_kv_heads > rpa::kPrefillRows)
+    return fail(RPA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per KV head",
+                s->num_q_heads / s->num_kv_heads, rpa::kPrefillRows);
+  if (!is_pow2(s->page_size) || s->page_size < 16)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two >= 16",
+                s->page_size);
+  if (s->num_pages <= 0) return fail(RPA_ERR_INVALID_ARGUMENT, "num_pages %d <= 0", s->num_pages);
+  if (s->max_pages_per_seq <= 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "max_pages_per_seq %d <= 0", s->max_pages_per_seq);
+  if (s->layout != RPA_LAYOUT_SEQ_MAJOR && s->layout != RPA_LAYOUT_HEAD_MAJOR)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "layout %d unknown", s->layout);
+  if (s->kernel < RPA_KERNEL_AUTO || s->kernel > RPA_KERNEL_MIXED)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "kernel %d unknown", s->kernel);
+  if (!need_lens) return RPA_OK;
+  if (!s->h_cu_q_lens || (s->num_seqs > 0 && !s->h_kv_lens))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "host mirrors of cu_q_lens / kv_lens are NULL");
+  if (s->h_cu_q_lens[0] != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "cu_q_lens[0] = %d, expected 0", s->h_cu_q_lens[0]);
+  const int Hkv_rows = s->layout == RPA_LAYOUT_HEAD_MAJOR ? s->num_kv_heads : 1;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
+    if (q_len < 0)
+      return fail(RPA_ERR_INVALID_ARGUMENT, "cu_q_lens decreases at sequence %d", b);
+    for (int g = 0; g < Hkv_rows; ++g) {
+      const int kv = kv_len_at(s, b, g);
+      if (kv < q_len)
+        return fail(RPA_ERR_INVALID_ARGUMENT,
+                    "sequence %d (kv head %d): kv_len %d < q_len %d (kv_len counts the new tokens)",
+                    b, g, kv, q_len);
+      if (cdiv(kv, s->page_size) > s->max_pages_per_seq)
+        return fail(RPA_ERR_INVALID_ARGUMENT,
+                    "sequence %d: kv_len %d needs %d pages > max_pages_per_seq %d", b, kv,
+                    cdiv(kv, s->page_size), s->max_pages_per_seq);
+    }
+  }
+  if (s->h_cu_q_lens[s->num_seqs] != s->total_q)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "cu_q_lens[B] = %d != total_q %d",
+                s->h_cu_q_lens[s->num_seqs], s->total_q);
+  return RPA_OK;
+}
+
+rpa_status check_device() {
+  static int arch_ok[64];  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(RPA_ERR_HIP, "hipGetDevice: %s (no usable GPU?)", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(RPA_ERR_UNSUPPORTED, "device index %d", dev);
+  if (arch_ok[dev] == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess)
+      return fail(RPA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    arch_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (arch_ok[dev] != 1)
+    return fail(RPA_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X); no code object for it", dev);
+  return RPA_OK;
+}
+
+struct Plan {
+  int kind = 0;         // RPA_KERNEL_DECODE / PREFILL / MIXED
+  int dec_rows_max = 0;
+  int split_dec = 1 << 30;
+  int split_pf = 1 << 30;
+  int pf_tokens = 1;
+  int n_dec_items = 0;
+  int n_pf_items = 0;
+  int max_nsplit = 1;
+};
+
+bool decode_class(const Plan &p, int q_len, int G) { return (long long)q_len * G <= p.dec_rows_max; }
+
+int splits_of(const Plan &p, int q_len, int G, int maxkv) {
+  const int split = decode_class(p, q_len, G) ? p.split_dec : p.split_pf;
+  return std::max(1, cdiv(maxkv, split));
+}
+
+// A split size in keys (a multiple of 64) that cuts `units` 64-key units into about
+// kTargetItems items, never giving one sequence more than kMaxSplits splits.
+int choose_split(long long units, int longest_kv, int min_keys) {
+  long long per_item = std::max<long long>(1, (units + kTargetItems - 1) / kTargetItems);
+  long long split = std::max<long long>(per_item * 64, min_keys);
+  const long long floor_for_cap = (long long)cdiv(cdiv(longest_kv, 64), kMaxSplits) * 64;
+  split = std::max(split, floor_for_cap);
+  return (int)std::min<long long>(split, 1 << 30);
+}
+
+Plan make_plan(const rpa_shape *s) {
+  Plan p;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  p.pf_tokens = std::max(1, rpa::kPrefillRows / G);
+  bool any_dec = false, any_pf = false;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
+    if (q_len == 0) continue;
+    if ((long long)q_len * G <= kDecodeRowsMax)
+      any_dec = true;
+    else
+      any_pf = true;
+  }
+  int kind = s->kernel;
+  if (kind == RPA_KERNEL_AUTO)
+    kind = any_dec && any_pf ? RPA_KERNEL_MIXED : (any_pf ? RPA_KERNEL_PREFILL : RPA_KERNEL_DECODE);
+  p.kind = kind;
+  p.dec_rows_max = kind == RPA_KERNEL_DECODE ? (1 << 30)
+                   : kind == RPA_KERNEL_PREFILL ? 0
+                                                : kDecodeRowsMax;
+  // Work in 64-key units of each class, to size the splits.
+  long long dec_units = 0, pf_units = 0;
+  int dec_longest = 0, pf_longest = 0;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
+    if (q_len == 0) continue;
+    const int kv = max_kv_len_host(s, b);
+    if (decode_class(p, q_len, G)) {
+      dec_units += (long long)s->num_kv_heads * cdiv((long long)q_len * G, rpa::kDecodeRows) * cdiv(kv, 64);
+      dec_longest = std::max(dec_longest, kv);
+    } else {
+      pf_units += (long long)s->num_kv_heads * cdiv(q_len, p.pf_tokens) * cdiv(kv, 64);
+      pf_longest = std::max(pf_longest, kv);
+    }
+  }
+  if (dec_units > 0) p.split_dec = choose_split(dec_units, dec_longest, 256);
+  if (pf_units > 0) {
+    if (kind == RPA_KERNEL_PREFILL)
+      // A prefill-only batch is compute-bound: split only when it has too few items to fill
+      // the chip; prefill units are 8x the rows of decode units, so aim 8x fewer items.
+      p.split_pf = choose_split(pf_units * 8, pf_longest, 1024);
+    else
+      p.split_pf = choose_split(pf_units * 8, pf_longest, 512);
+  }
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
+    if (q_len == 0) continue;
+    const int kv = max_kv_len_host(s, b);
+    const int ns = splits_of(p, q_len, G, kv);
+    p.max_nsplit = std::max(p.max_nsplit, ns);
+    if (decode_class(p, q_len, G))
+      p.n_dec_items += s->num_kv_heads * cdiv((long long)q_len * G, rpa::kDecodeRows) * ns;
+    else
+      p.n_pf_items += s->num_kv_heads * cdiv(q_len, p.pf_tokens) * ns;
+  }
+  return p;
+}
+
+size_t workspace_bytes_for(const rpa_shape *s, const Plan &p) {
+  if (p.max_nsplit <= 1) return 0;
+  const size_t rows = (size_t)p.max_nsplit * s->total_q * s->num_q_heads;
+  return rows * (size_t)(s->head_dim + 2) * sizeof(float);
+}
+
+void fill_layout(const rpa_shape *s, int64_t &page_stride, int64_t &slot_stride,
+                 int64_t &head_stride, int32_t &bt_seq, int32_t &bt_head, int32_t &kvl_seq,
+                 int32_t &kvl_head) {
+  const int64_t D = s->head_dim, S = s->page_size, Hkv = s->num_kv_heads;
+  if (s->layout == RPA_LAYOUT_SEQ_MAJOR) {
+    page_stride = S * Hkv * D;
+    slot_stride = Hkv * D;
+    head_stride = D;
+    bt_seq = s->max_pages_per_seq;
+    bt_head = 0;
+    kvl_seq = 1;
+    kvl_head = 0;
+  } else {
+    page_stride = S * D;
+    slot_stride = D;
+    head_stride = 0;
+    bt_seq = (int32_t)(Hkv * s->max_pages_per_seq);
+    bt_head = s->max_pages_per_seq;
+    kvl_seq = (int32_t)Hkv;
+    kvl_head = 1;
+  }
+}
+
+rpa_status write_kv_impl(const rpa_shape *s, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, const int32_t *tables, const int32_t *cu, const int32_t *kvl,
+                         hipStream_t stream) {
+  rpa::WriteArgs w{};
+  w.k_new = static_cast<const uint16_t *>(k_new);
+  w.v_new = static_cast<const uint16_t *>(v_new);
+  w.k_cache = static_cast<uint16_t *>(k_cache);
+  w.v_cache = static_cast<uint16_t *>(v_cache);
+  w.tables = tables;
+  w.cu_q_lens = cu;
+  w.kv_lens = kvl;
+  w.B = s->num_seqs;
+  w.T = s->total_q;
+  w.Hkv = s->num_kv_heads;
+  w.page_shift = ilog2(s->page_size);
+  fill_layout(s, w.page_stride, w.slot_stride, w.head_stride, w.bt_seq_stride, w.bt_head_stride,
+              w.kvl_seq_stride, w.kvl_head_stride);
+  hipError_t e = rpa::launch_write_kv(w, s->head_dim, stream);
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "write_kv launch: %s", hipGetErrorString(e));
+  return RPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rpa_status rpa_write_kv(const rpa_shape *shape, const void *k_new, const void *v_new,
+                        void *k_cache, void *v_cache, const int32_t *block_tables,
+                        const int32_t *cu_q_lens, const int32_t *kv_lens, void *stream) {
+  rpa_status st = validate(shape, true);
+  if (st != RPA_OK) return st;
+  if (shape->total_q == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !cu_q_lens || !kv_lens)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_write_kv: a device pointer is NULL");
+  st = check_device();
+  if (st != RPA_OK) return st;
+  st = write_kv_impl(shape, k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens,
+                     static_cast<hipStream_t>(stream));
+  return st == RPA_OK ? ok() : st;
+}
+
+size_t rpa_attention_workspace_size(const rpa_shape *shape) {
+  if (validate(shape, true) != RPA_OK) return (size_t)-1;
+  if (shape->total_q == 0) return 0;
+  return workspace_bytes_for(shape, make_plan(shape));
+}
+
+int32_t rpa_select_kernel(const rpa_shape *shape) {
+  if (validate(shape, true) != RPA_OK) return -1;
+  return make_plan(shape).kind;
+}
+
+rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
+                         const int32_t *block_tables, const int32_t *cu_q_lens,
+                         const int32_t *kv_lens, float scale, const void *k_new,
+                         const void *v_new, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  rpa_status st = validate(shape, true);
+  if (st != RPA_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "scale %g must be finite and > 0", (double)scale);
+  if (shape->total_q == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !cu_q_lens || !kv_lens || !out)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_attention: a device pointer is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "k_new and v_new must both be given or both be NULL");
+  const Plan p = make_plan(shape);
+  const size_t need = workspace_bytes_for(shape, p);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(RPA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
+                workspace_bytes, need);
+  st = check_device();
+  if (st != RPA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (k_new) {
+    st = write_kv_impl(shape, k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, hs);
+    if (st != RPA_OK) return st;
+  }
+  rpa::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(k_cache);
+  a.v_cache = static_cast<const uint16_t *>(v_cache);
+  a.out = static_cast<uint16_t *>(out);
+  a.tables = block_tables;
+  a.cu_q_lens = cu_q_lens;
+  a.kv_lens = kv_lens;
+  const size_t o_bytes = (size_t)p.max_nsplit * shape->total_q * shape->num_q_heads *
+                         shape->head_dim * sizeof(float);
+  a.part_o = need ? static_cast<float *>(workspace) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes) : nullptr;
+  a.B = shape->num_seqs;
+  a.T = shape->total_q;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.page_shift = ilog2(shape->page_size);
+  fill_layout(shape, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride,
+              a.bt_head_stride, a.kvl_seq_stride, a.kvl_head_stride);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dec_rows_max = p.dec_rows_max;
+  a.split_dec = p.split_dec;
+  a.split_pf = p.split_pf;
+  a.pf_tokens = p.pf_tokens;
+  a.n_pf_items = p.n_pf_items;
+  const int n_items = p.n_pf_items + p.n_dec_items;
+  hipError_t e = rpa::launch_attention(a, shape->head_dim, static_cast<rpa::AttnKernel>(p.kind),
+                                       n_items, p.max_nsplit > 1, hs);
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+rpa_status rpa_build_union_tables(const uint8_t *mask, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t num_q_blocks, int32_t num_kv_blocks,
+                                  const int32_t *base_tables, int32_t past, int32_t kv_len,
+                                  int32_t page_size, int32_t *out_tables, int32_t *out_counts,
+                                  int32_t *out_kv_lens, void *stream) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT,
+                "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_q_blocks <= 0 || num_kv_blocks <= 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "num_q_blocks %d and num_kv_blocks %d must be > 0",
+                num_q_blocks, num_kv_blocks);
+  if (num_kv_blocks > rpa::kMaxUnionKvBlocks)
+    return fail(RPA_ERR_UNSUPPORTED, "num_kv_blocks %d > %d", num_kv_blocks,
+                rpa::kMaxUnionKvBlocks);
+  if (!is_pow2(page_size) || page_size < 16)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two >= 16", page_size);
+  if (past < 0 || kv_len <= past)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "need 0 <= past (%d) < kv_len (%d)", past, kv_len);
+  if (cdiv(kv_len, page_size) > num_kv_blocks)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "kv_len %d needs %d blocks > num_kv_blocks %d", kv_len,
+                cdiv(kv_len, page_size), num_kv_blocks);
+  if (!mask || !base_tables || !out_tables || !out_counts || !out_kv_lens)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_build_union_tables: a device pointer is NULL");
+  rpa_status st = check_device();
+  if (st != RPA_OK) return st;
+  rpa::UnionArgs u{};
+  u.mask = mask;
+  u.base = base_tables;
+  u.out_tables = out_tables;
+  u.out_counts = out_counts;
+  u.out_kv_lens = out_kv_lens;
+  u.Hq = num_q_heads;
+  u.Hkv = num_kv_heads;
+  u.nQB = num_q_blocks;
+  u.nKB = num_kv_blocks;
+  u.past = past;
+  u.kv_len = kv_len;
+  u.page_size = page_size;
+  hipError_t e = rpa::launch_union_tables(u, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "union tables launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char *rpa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

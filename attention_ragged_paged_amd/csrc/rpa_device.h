@@ -1,0 +1,156 @@
+// Device-side building blocks shared by the gfx950 kernels of librpa.
+//
+// Nothing here is used by the CPU oracle; the GPU path and the oracle share no code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define RPA_LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;        // every attention workgroup: 4 wave64s
+constexpr int kDecodeRows = 16;      // query rows per decode work item (one 16x16 MFMA tile)
+constexpr int kPrefillRows = 128;    // query rows per prefill work item (4 waves x 32)
+constexpr int kPrefillKeys = 64;     // keys per prefill KV tile
+
+// Everything the attention kernels need, passed by value as the kernel argument.
+struct AttnArgs {
+  const uint16_t *q;        // [T][Hq][D] bf16
+  const uint16_t *k_cache;  // paged cache, see strides
+  const uint16_t *v_cache;
+  uint16_t *out;            // [T][Hq][D] bf16
+  const int32_t *tables;
+  const int32_t *cu_q_lens; // [B + 1]
+  const int32_t *kv_lens;
+  float *part_o;            // [max_nsplit][T][Hq][D] unnormalised partial outputs
+  float *part_ml;           // [max_nsplit][T][Hq][2] running max (log2 units) and sum
+  int32_t B, T, Hq, Hkv, G;
+  int32_t page_shift;       // log2(page size)
+  int64_t page_stride, slot_stride, head_stride;  // cache element strides
+  int32_t bt_seq_stride, bt_head_stride;          // table entry (b, g, i) = tables[b*seq + g*head + i]
+  int32_t kvl_seq_stride, kvl_head_stride;        // kv_len(b, g) = kv_lens[b*seq + g*head]
+  float scale_log2;         // softmax scale * log2(e)
+  int32_t dec_rows_max;     // a sequence is decode-class iff q_len * G <= dec_rows_max
+  int32_t split_dec;        // keys per split of a decode-class sequence (multiple of 64)
+  int32_t split_pf;         // keys per split of a prefill-class sequence (multiple of 64)
+  int32_t pf_tokens;        // tokens per prefill tile: kPrefillRows / G (at least 1)
+  int32_t n_pf_items;       // mixed kernel: blocks [0, n_pf_items) are prefill items
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int kv_len_of(const AttnArgs &a, int b, int g) {
+  return a.kv_lens[b * a.kvl_seq_stride + g * a.kvl_head_stride];
+}
+
+// Longest kv_len over the KV heads of sequence b (all equal in the sequence-major layout).
+__device__ __forceinline__ int max_kv_len(const AttnArgs &a, int b) {
+  int m = a.kv_lens[b * a.kvl_seq_stride];
+  if (a.kvl_head_stride != 0)
+    for (int g = 1; g < a.Hkv; ++g) m = max(m, a.kv_lens[b * a.kvl_seq_stride + g]);
+  return m;
+}
+
+__device__ __forceinline__ bool is_decode_class(const AttnArgs &a, int q_len) {
+  return q_len * a.G <= a.dec_rows_max;
+}
+
+__device__ __forceinline__ int ceil_div(int x, int y) { return (x + y - 1) / y; }
+
+// Number of KV splits of sequence b (the same formula on the host and in the merge).
+__device__ __forceinline__ int num_splits(const AttnArgs &a, int b, int q_len) {
+  int split = is_decode_class(a, q_len) ? a.split_dec : a.split_pf;
+  return max(1, ceil_div(max_kv_len(a, b), split));
+}
+
+struct ItemRef {
+  int b;    // sequence, or -1 when the id is past the last item
+  int rem;  // index of the item within its sequence
+};
+
+// Maps a work-item id onto (sequence, index within the sequence), where sequence b owns
+// count(b) consecutive ids.  Every lane of the wave computes the same answer: lanes take
+// 64 sequences at a time, a wave-wide inclusive scan gives the running offsets.
+template <class CountFn>
+__device__ __forceinline__ ItemRef find_item(int id, int B, CountFn count) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int c = b < B ? count(b) : 0;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (id < base + total) {
+      const unsigned long long hit = __ballot(base + incl > id);
+      const int l = __ffsll((long long)hit) - 1;
+      const int excl = __shfl(incl - c, l);
+      return {b0 + l, id - base - excl};
+    }
+    base += total;
+  }
+  return {-1, 0};
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16-byte chunk c of row r of an LDS tile stored row-major with D bf16 per row.  The
+// chunk index is XOR-swizzled with the row so that the same chunk of 16 consecutive rows
+// falls in different LDS banks (column reads of the MFMA operand layouts are conflict-free).
+template <int D>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  constexpr int kChunks = D / 8;
+  return c ^ (r & (kChunks - 1));
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off(int r, int c) {  // offset in bf16 elements
+  return r * D + swz_chunk<D>(r, c) * 8;
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// names 8 bytes holding row i/4, columns 4*(i%4) .. 4*(i%4)+3 of a 4 x 16 block of bf16;
+// it receives column i, i.e. the 4 elements (row 0..3, column i).
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RPA_LDS s16x4 *)(p));
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x16(const s16x4 &a, const s16x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+}  // namespace rpa

@@ -1,0 +1,51 @@
+// Host-visible launch entry points of the gfx950 kernels (used by the C ABI in capi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpa {
+
+struct AttnArgs;
+
+struct WriteArgs {
+  const uint16_t *k_new;  // [T][Hkv][D] bf16
+  const uint16_t *v_new;
+  uint16_t *k_cache;
+  uint16_t *v_cache;
+  const int32_t *tables;
+  const int32_t *cu_q_lens;
+  const int32_t *kv_lens;
+  int32_t B, T, Hkv;
+  int32_t page_shift;
+  int64_t page_stride, slot_stride, head_stride;
+  int32_t bt_seq_stride, bt_head_stride;
+  int32_t kvl_seq_stride, kvl_head_stride;
+};
+
+enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };
+
+hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
+
+// Runs the attention kernel of the given kind over n_items work items, then the split-K
+// merge when any sequence is split (merge_rows = T * Hq rows, 0 = no merge).
+hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_items, bool merge,
+                            hipStream_t stream);
+
+struct UnionArgs {
+  const uint8_t *mask;       // [Hq][nQB][nKB]
+  const int32_t *base;       // [Hkv][nKB]
+  int32_t *out_tables;       // [Hkv][nKB]
+  int32_t *out_counts;       // [Hkv]
+  int32_t *out_kv_lens;      // [Hkv]
+  int32_t Hq, Hkv, nQB, nKB;
+  int32_t past, kv_len, page_size;
+};
+
+// Largest num_kv_blocks the builder accepts (its compaction pass keeps one flag byte per
+// block in LDS).
+constexpr int kMaxUnionKvBlocks = 32768;
+
+hipError_t launch_union_tables(const UnionArgs &a, hipStream_t stream);
+
+}  // namespace rpa

@@ -1,0 +1,168 @@
+/*
+ * rpa.h -- C ABI of the ragged paged attention library (librpa.so, gfx950 only).
+ *
+ * What it computes.  Causal grouped-query attention over a ragged batch that
+ * mixes decode sequences (a few new tokens) and chunked-prefill sequences (many
+ * new tokens).  K and V are read in place from a paged cache through
+ * per-sequence block tables, and the new tokens' K/V rows can be scattered into
+ * their pages in the same call.  This follows the method of "Ragged Paged
+ * Attention: A High-Performance and Flexible LLM Inference Kernel for TPU"
+ * (summary card, "Key ideas": ragged paged KV, cache writes fused with
+ * attention, separate decode / prefill / mixed kernels) and the interface
+ * conventions of ONNX Runtime PR 31727, "[WebGPU] Optimized PagedAttention
+ * implementation (2/n)" (packed varlen Q with cumulative lengths, block tables,
+ * in-place cache update, token_count == 0 is a no-op).  The block-union variant
+ * follows "CompactAttention: Accelerating Chunked Prefill with Block-Union KV
+ * Selection" ("Core claim", Figures 3 and 4).
+ *
+ * Conventions shared by every entry point.
+ *   - bf16 means bfloat16 storage; all accumulation is fp32.
+ *   - All arrays are row-major and densely packed.  Pointers named d_* or
+ *     passed as tensor data are DEVICE pointers; h_* pointers are HOST pointers.
+ *   - kv_len of a sequence counts all of its keys INCLUDING the new tokens; the
+ *     new tokens are the last q_len positions: token t sits at position
+ *     past + t (past = kv_len - q_len) and attends to keys 0 .. past + t
+ *     (bottom-right causal alignment, the seqlens_q fix of the ONNX Runtime PR).
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - Every buffer belongs to the caller.  The library allocates no device
+ *     memory: scratch space is the caller's workspace.  Caches are updated in
+ *     place.  q, out, k_new and v_new must not alias the caches or each other.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Host arrays are read only during the call.
+ *   - No call aborts or throws.  A non-zero status comes with a message from
+ *     rpa_last_error() (thread-local).  Device contents are preconditions that
+ *     are NOT checked: block-table entries of every block a sequence uses must
+ *     lie in [0, num_pages), and slots written for different sequences must be
+ *     disjoint.
+ */
+#ifndef RPA_H
+#define RPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rpa_status {
+  RPA_OK = 0,
+  RPA_ERR_INVALID_ARGUMENT = 1,   /* malformed shape, lengths, pointers or scale */
+  RPA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, device, group size */
+  RPA_ERR_WORKSPACE_TOO_SMALL = 3,
+  RPA_ERR_HIP = 4                 /* a HIP runtime call failed (message names it) */
+} rpa_status;
+
+/* Cache layouts.
+ *   SEQ_MAJOR  (the ONNX Runtime op's paged layout): k_cache, v_cache
+ *              [num_pages][page_size][Hkv][D]; one block table row per sequence
+ *              block_tables[B][max_pages_per_seq]; kv_lens[B].
+ *   HEAD_MAJOR (the KV-head-major layout of CompactAttention, Figure 4: each
+ *              page holds one KV head, so every KV head has its own table):
+ *              k_cache, v_cache [num_pages][page_size][D];
+ *              block_tables[B][Hkv][max_pages_per_seq]; kv_lens[B][Hkv]. */
+enum { RPA_LAYOUT_SEQ_MAJOR = 0, RPA_LAYOUT_HEAD_MAJOR = 1 };
+
+/* Kernel selection.  AUTO picks from the batch composition: every sequence
+ * decode-class -> DECODE, every one prefill-class -> PREFILL, both -> MIXED
+ * (a sequence is decode-class when q_len * (Hq / Hkv) <= 16).  The forced
+ * kinds exist for cross-checks; each kernel is correct for any batch. */
+enum { RPA_KERNEL_AUTO = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_PREFILL = 2, RPA_KERNEL_MIXED = 3 };
+
+typedef struct rpa_shape {
+  int32_t num_seqs;           /* B >= 0 */
+  int32_t total_q;            /* T = cu_q_lens[B] */
+  int32_t num_q_heads;        /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t page_size;          /* S: a power of two >= 16 (the PR's block_size rule) */
+  int32_t num_pages;          /* P: pages in each cache */
+  int32_t max_pages_per_seq;  /* row length of the block table */
+  int32_t layout;             /* RPA_LAYOUT_* */
+  int32_t kernel;             /* RPA_KERNEL_* (AUTO in normal use) */
+  const int32_t *h_cu_q_lens; /* host mirror of cu_q_lens, [B + 1] */
+  const int32_t *h_kv_lens;   /* host mirror of kv_lens, [B] or [B][Hkv] */
+} rpa_shape;
+
+/*
+ * rpa_write_kv -- scatter the new tokens' K/V rows into their pages.
+ * Defined by the scatter program of the ONNX Runtime PR (Phase 1b.1 commit
+ * note): for token t of sequence b and KV head g, pos = past_b + t,
+ * page = table(b, g)[pos / page_size], slot = pos % page_size, and the D values
+ * of k_new[cu_q_lens[b] + t][g] (likewise v_new) are copied into that slot.
+ *   k_new, v_new  device bf16 [T][Hkv][D]
+ *   k_cache, v_cache  device bf16, layout per shape->layout, written in place
+ *   block_tables, cu_q_lens, kv_lens  device int32 copies of the table and of
+ *                 the host mirrors in *shape
+ * Bit-exact copy; no other cache byte is touched.  T == 0 returns RPA_OK.
+ */
+rpa_status rpa_write_kv(const rpa_shape *shape, const void *k_new, const void *v_new,
+                        void *k_cache, void *v_cache, const int32_t *block_tables,
+                        const int32_t *cu_q_lens, const int32_t *kv_lens, void *stream);
+
+/* Bytes of device workspace rpa_attention needs for this shape (split-K
+ * partials).  0 is a valid answer.  Returns (size_t)-1 on an invalid shape. */
+size_t rpa_attention_workspace_size(const rpa_shape *shape);
+
+/* The kernel rpa_attention will run for this shape (RPA_KERNEL_DECODE /
+ * PREFILL / MIXED), or -1 on an invalid shape.  Host-only, no device call. */
+int32_t rpa_select_kernel(const rpa_shape *shape);
+
+/*
+ * rpa_attention -- ragged paged causal GQA attention.
+ *   q             device bf16 [T][Hq][D]
+ *   k_cache, v_cache  device bf16 caches (layout per shape->layout)
+ *   block_tables  device int32, see the layouts above; unused entries may be -1
+ *   cu_q_lens     device int32 [B + 1], non-decreasing from 0 to T
+ *   kv_lens       device int32 [B] (or [B][Hkv] for HEAD_MAJOR)
+ *   scale         softmax scale applied to q.k (finite, > 0), e.g. 1/sqrt(D)
+ *   k_new, v_new  NULL, or device bf16 [T][Hkv][D]: when given, they are first
+ *                 scattered into the caches exactly as rpa_write_kv does, on
+ *                 the same stream, and the attention sees them
+ *   out           device bf16 [T][Hq][D], fully written
+ *   workspace     device scratch of >= rpa_attention_workspace_size(shape) bytes
+ *                 (may be NULL when that size is 0); its contents on entry do
+ *                 not matter and are clobbered
+ * For each row: out = softmax(scale * q K^T over keys 0 .. past + t) V, fp32
+ * accumulate, rounded to bf16 (round to nearest even).  Sequences with
+ * q_len == 0 are skipped; T == 0 returns RPA_OK without a launch.
+ */
+rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
+                         const int32_t *block_tables, const int32_t *cu_q_lens,
+                         const int32_t *kv_lens, float scale, const void *k_new,
+                         const void *v_new, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * rpa_build_union_tables -- per-KV-head block tables of one sequence's chunk
+ * from a per-head 2D block mask (CompactAttention, "Core claim" and Figure 3:
+ * union over query blocks, then over the query heads of each GQA group).
+ *   mask          device uint8 [Hq][num_q_blocks][num_kv_blocks]; nonzero =
+ *                 query block qb of head h selects KV block kb
+ *   base_tables   device int32 [Hkv][num_kv_blocks]: physical page of every
+ *                 logical block of each KV head (KV-head-major pages)
+ *   past, kv_len  the chunk covers positions [past, kv_len)
+ *   out_tables    device int32 [Hkv][num_kv_blocks]: selected blocks' pages in
+ *                 ascending block order, then -1
+ *   out_counts    device int32 [Hkv]: number of selected blocks
+ *   out_kv_lens   device int32 [Hkv]: keys of the compacted sequence
+ * The chunk's own blocks [past / page_size, (kv_len - 1) / page_size] are always
+ * selected and blocks at or beyond ceil(kv_len / page_size) never are, so the
+ * chunk's queries are the last (kv_len - past) positions of every compacted
+ * sequence and rpa_attention (HEAD_MAJOR, out_tables, out_kv_lens) runs causal
+ * attention over the selected pages in place.  Deterministic and bit-exact.
+ */
+rpa_status rpa_build_union_tables(const uint8_t *mask, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t num_q_blocks, int32_t num_kv_blocks,
+                                  const int32_t *base_tables, int32_t past, int32_t kv_len,
+                                  int32_t page_size, int32_t *out_tables, int32_t *out_counts,
+                                  int32_t *out_kv_lens, void *stream);
+
+/* Human-readable message for the last non-OK status on this thread ("" if none). */
+const char *rpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H */

@@ -1,0 +1,103 @@
+"""Helpers shared by the GPU tests: move a seeded batch to the device, run the HIP path
+through the C ABI, and compare with the CPU oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import attention_ragged_paged_amd as rpa
+import oracle
+from attention_ragged_paged_amd import workloads as wl
+
+ATOL = 2e-2   # max-abs bound for bf16 inputs, fp32 accumulation, bf16 output
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def i32_dev(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr, np.int32)).cuda()
+
+
+def to_host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_host_f32(t):
+    return t.float().cpu().numpy()
+
+
+class Dev:
+    """Device copies of a RaggedBatch."""
+
+    def __init__(self, b: wl.RaggedBatch):
+        self.b = b
+        self.q = bf16_dev(b.q)
+        self.k_new = bf16_dev(b.k_new)
+        self.v_new = bf16_dev(b.v_new)
+        self.k_cache = bf16_dev(b.k_cache)
+        self.v_cache = bf16_dev(b.v_cache)
+        self.tables = i32_dev(b.block_tables)
+        self.cu = i32_dev(b.cu_q_lens)
+        self.kvl = i32_dev(b.kv_lens)
+        self.cu_h = torch.from_numpy(np.ascontiguousarray(b.cu_q_lens, np.int32))
+        self.kvl_h = torch.from_numpy(np.ascontiguousarray(b.kv_lens, np.int32))
+
+    def attention(self, fused_write=True, kernel=rpa.KERNEL_AUTO, tables=None, kv_lens=None,
+                  kv_lens_host=None):
+        out = rpa.attention(self.q, self.k_cache, self.v_cache,
+                            self.tables if tables is None else tables, self.cu,
+                            self.kvl if kv_lens is None else kv_lens, self.b.scale,
+                            k_new=self.k_new if fused_write else None,
+                            v_new=self.v_new if fused_write else None,
+                            cu_q_lens_host=self.cu_h,
+                            kv_lens_host=self.kvl_h if kv_lens_host is None else kv_lens_host,
+                            kernel=kernel)
+        torch.cuda.synchronize()
+        return out
+
+    def write(self):
+        rpa.write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.tables, self.cu,
+                     self.kvl, cu_q_lens_host=self.cu_h, kv_lens_host=self.kvl_h)
+        torch.cuda.synchronize()
+
+
+def oracle_after_write(b: wl.RaggedBatch):
+    """Caches after the oracle's scatter of the new tokens."""
+    return oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new, b.k_cache,
+                           b.v_cache, b.page_size, layout=b.layout)
+
+
+def sample_rows(b: wl.RaggedBatch, n, seed=0):
+    """(token, head) rows spread over every sequence: first/last tokens, tile edges, random."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    Hq = b.num_q_heads
+    for s in range(b.num_seqs):
+        q0, q1 = int(b.cu_q_lens[s]), int(b.cu_q_lens[s + 1])
+        if q1 == q0:
+            continue
+        for t in {q0, q1 - 1, (q0 + q1) // 2}:
+            rows.add((t, int(rng.integers(Hq))))
+            rows.add((t, 0))
+            rows.add((t, Hq - 1))
+    T = b.total_q
+    while len(rows) < n:
+        rows.add((int(rng.integers(T)), int(rng.integers(Hq))))
+    return np.array(sorted(rows), np.int32)
+
+
+def compare(got_f32, want_f64, label):
+    err = np.abs(got_f32.astype(np.float64) - want_f64)
+    finite = np.isfinite(got_f32).all()
+    mx = float(err.max()) if err.size else 0.0
+    say(f"  {label}: max-abs {mx:.3e} mean-abs {float(err.mean()) if err.size else 0:.3e}")
+    assert finite, f"{label}: non-finite output"
+    assert mx <= ATOL, f"{label}: max-abs {mx} > {ATOL}"
+    return mx

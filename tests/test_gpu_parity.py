@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Cache writes and union tables must match bit for bit; attention outputs within max-abs 2e-2
+(bf16 inputs, fp32 accumulation, bf16 output).  Small cases compare every output element;
+the full-size workloads compare sampled rows that the oracle computes one by one.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import attention_ragged_paged_amd as rpa
+import oracle
+from attention_ragged_paged_amd import workloads as wl
+from tests.gpu_util import (Dev, bf16_dev, compare, i32_dev, oracle_after_write, sample_rows, say,
+                            to_host_bits, to_host_f32)
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = [rpa.KERNEL_AUTO, rpa.KERNEL_DECODE, rpa.KERNEL_PREFILL, rpa.KERNEL_MIXED]
+
+
+def _full_check(b, kernel=rpa.KERNEL_AUTO, fused=True, label=""):
+    d = Dev(b)
+    if not fused:
+        d.write()
+    out = d.attention(fused_write=fused, kernel=kernel)
+    kc, vc = oracle_after_write(b)
+    assert np.array_equal(to_host_bits(d.k_cache), kc), f"{label}: K cache differs"
+    assert np.array_equal(to_host_bits(d.v_cache), vc), f"{label}: V cache differs"
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                           b.page_size, b.num_kv_heads, layout=b.layout)
+    return compare(to_host_f32(out), ref, label)
+
+
+# ------------------------------------------------------------------------------ write ----
+
+@pytest.mark.parametrize("layout", [wl.SEQ_MAJOR, wl.HEAD_MAJOR])
+@pytest.mark.parametrize("D", [64, 128])
+def test_write_kv_bit_exact(layout, D):
+    say(f"write_kv layout={layout} D={D}")
+    b = wl.ragged_batch("w", [1, 7, 0, 33, 16], [17, 23, 5, 100, 16], 8, 2, D, 16, 40, 21,
+                        layout=layout)
+    d = Dev(b)
+    d.write()
+    kc, vc = oracle_after_write(b)
+    assert np.array_equal(to_host_bits(d.k_cache), kc)
+    assert np.array_equal(to_host_bits(d.v_cache), vc)
+
+
+# ------------------------------------------------------------------- tiny ragged batch ---
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_tiny_ragged_every_kernel(kernel):
+    say(f"tiny_ragged kernel={kernel}")
+    _full_check(wl.tiny_ragged(), kernel=kernel, label=f"tiny kernel={kernel}")
+
+
+def test_tiny_ragged_separate_write():
+    say("tiny_ragged separate write")
+    _full_check(wl.tiny_ragged(), fused=False, label="tiny write-then-attend")
+
+
+def _matrix():
+    cases = []
+    q_sets = [[1], [4], [16], [32], [48], [1, 4], [0, 16, 1], [32, 1, 0, 3], [48, 16, 1, 4]]
+    heads = [(4, 4), (8, 2), (14, 2), (32, 8)]
+    pages = [16, 32, 64, 128, 256]
+    rng = np.random.default_rng(99)
+    for i, (qs, (Hq, Hkv), S, D) in enumerate(itertools.product(q_sets, heads, pages, [64, 128])):
+        if rng.random() > 0.12:
+            continue
+        past = [int(rng.integers(0, 300)) for _ in qs]
+        cases.append((qs, past, Hq, Hkv, S, D, i))
+    return cases
+
+
+@pytest.mark.parametrize("qs,past,Hq,Hkv,S,D,i", _matrix())
+def test_ragged_matrix(qs, past, Hq, Hkv, S, D, i):
+    kv = [q + p for q, p in zip(qs, past)]
+    pool = sum((k + S - 1) // S for k in kv) + 3
+    scale = 0.05 + 0.01 * (i % 7)   # explicit non-default scales
+    b = wl.ragged_batch("m", qs, kv, Hq, Hkv, D, S, pool, 1000 + i, scale=scale)
+    for kernel in KERNELS:
+        say(f"matrix case {i}: q={qs} past={past} heads={Hq}/{Hkv} S={S} D={D} kernel={kernel}")
+        _full_check(b, kernel=kernel, label=f"case {i} kernel {kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_nan_in_unowned_slots_does_not_leak(kernel):
+    """Unused pages and the tail slots past each sequence's kv_len hold NaN."""
+    say(f"nan poison kernel={kernel}")
+    b = wl.ragged_batch("nan", [1, 5, 40, 1], [33, 21, 75, 250], 8, 2, 128, 16, 40, 31,
+                        poison_unused=True)
+    _full_check(b, kernel=kernel, label=f"nan kernel={kernel}")
+
+
+def test_mixed_order_does_not_matter():
+    """Reordering the sequences of a mixed batch permutes per-sequence results only."""
+    say("mixed order")
+    b = wl.ragged_batch("ord", [200, 1, 1, 3], [700, 90, 300, 40], 32, 8, 128, 16, 120, 41)
+    _full_check(b, label="mixed order A")
+    perm = [2, 0, 3, 1]
+    qs = np.diff(b.cu_q_lens)
+    b2 = wl.ragged_batch("ord2", qs[perm], b.kv_lens[perm], 32, 8, 128, 16, 120, 41)
+    _full_check(b2, label="mixed order B")
+
+
+def test_long_decode_sequence_many_chunks():
+    """One decode sequence long enough that a wave walks more than 64 chunks of its split."""
+    say("long decode 300k")
+    b = wl.ragged_batch("long", [1, 2], [300000, 5000], 4, 1, 128, 16, 19100, 51)
+    d = Dev(b)
+    out = d.attention()
+    kc, vc = oracle_after_write(b)
+    rows = np.array([[0, 0], [0, 3], [1, 1], [2, 2]], np.int32)
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale, 16, 1,
+                           rows=rows)
+    got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
+    compare(got, ref, "long decode")
+
+
+# --------------------------------------------------------------- full-size workloads ----
+
+def _sampled(b, n_rows, label, kernel=rpa.KERNEL_AUTO, check_cache=True):
+    d = Dev(b)
+    out = d.attention(kernel=kernel)
+    kc, vc = oracle_after_write(b)
+    if check_cache:
+        assert np.array_equal(to_host_bits(d.k_cache), kc), f"{label}: K cache differs"
+        assert np.array_equal(to_host_bits(d.v_cache), vc), f"{label}: V cache differs"
+    rows = sample_rows(b, n_rows)
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                           b.page_size, b.num_kv_heads, layout=b.layout, rows=rows)
+    got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
+    return compare(got, ref, label)
+
+
+def test_llama3_decode_full_size():
+    say("llama3_decode full size (64 seqs, kv U[512,4096], 20k-page pool)")
+    _sampled(wl.llama3_decode(), 512, "llama3 decode")
+
+
+def test_llama3_prefill_full_size():
+    say("llama3_prefill full size (4 x 2048, page 64)")
+    _sampled(wl.llama3_prefill(), 256, "llama3 prefill")
+
+
+def test_mixed_chunked_full_size():
+    say("mixed_chunked full size (512 @ 8192 + 96 decodes, page 16)")
+    b = wl.mixed_chunked()
+    d = Dev(b)
+    assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_MIXED
+    del d
+    _sampled(b, 400, "mixed chunked")
+
+
+# ------------------------------------------------------------------ union tables -------
+
+@pytest.mark.parametrize("seed,Hq,Hkv,nQB,nKB,S,past,kv_len,dens", [
+    (0, 8, 2, 4, 24, 16, 320, 370, 0.2),
+    (1, 4, 4, 3, 100, 32, 1000, 1070, 0.05),   # G = 1, unaligned block count
+    (2, 32, 8, 64, 2048, 64, 126976, 131072, 0.1),
+    (3, 28, 4, 5, 4096, 16, 65000, 65536, 0.0),
+])
+def test_union_tables_bit_exact(seed, Hq, Hkv, nQB, nKB, S, past, kv_len, dens):
+    say(f"union tables seed={seed}")
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((Hq, nQB, nKB)) < dens).astype(np.uint8)
+    base = rng.permutation(Hkv * nKB).astype(np.int32).reshape(Hkv, nKB)
+    t, c, k = rpa.build_union_tables(torch.from_numpy(mask).cuda(), i32_dev(base), past, kv_len, S)
+    torch.cuda.synchronize()
+    et, ec, ek, _ = oracle.union_tables(mask, base, past, kv_len, S)
+    assert np.array_equal(t.cpu().numpy(), et)
+    assert np.array_equal(c.cpu().numpy(), ec)
+    assert np.array_equal(k.cpu().numpy(), ek)
+
+
+@pytest.mark.parametrize("column_shared", [False, True])
+def test_block_union_sparse_full_size(column_shared):
+    """Union tables built on the GPU, chunk K/V written through the base tables, then causal
+    attention over the selected KV-head-major pages; sampled rows against the oracle's
+    position-wise sparse attention."""
+    say(f"block_union_sparse full size column_shared={column_shared}")
+    b = wl.block_union_sparse(column_shared=column_shared)
+    past, ctx = b.extra["past"], b.extra["context"]
+    d = Dev(b)
+    mask_d = torch.from_numpy(b.extra["mask"]).cuda()
+    t, c, kvl = rpa.build_union_tables(mask_d, d.tables[0], past, ctx, b.page_size)
+    torch.cuda.synchronize()
+    et, ec, ek, sel = oracle.union_tables(b.extra["mask"], b.block_tables[0], past, ctx,
+                                          b.page_size)
+    assert np.array_equal(t.cpu().numpy(), et) and np.array_equal(kvl.cpu().numpy(), ek)
+    say(f"  union density per KV head: {np.round(ec / (ctx // b.page_size), 3).tolist()}")
+    d.write()
+    out = d.attention(fused_write=False, tables=t[None].contiguous(),
+                      kv_lens=kvl[None].contiguous(),
+                      kv_lens_host=torch.from_numpy(ek[None].copy()))
+    kc, vc = oracle_after_write(b)
+    rows = sample_rows(b, 96)
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                           b.page_size, b.num_kv_heads, layout=wl.HEAD_MAJOR,
+                           block_allowed=sel[None], rows=rows)
+    got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
+    compare(got, ref, f"sparse column_shared={column_shared}")
