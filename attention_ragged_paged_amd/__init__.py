@@ -15,6 +15,8 @@ from ._rpa import (  # noqa: F401
     KERNEL_PREFILL,
     LAYOUT_HEAD_MAJOR,
     LAYOUT_SEQ_MAJOR,
+    PreparedAttention,
+    PreparedWriteKV,
     RpaError,
     attention,
     build_union_tables,

@@ -226,3 +226,53 @@ def build_union_tables(mask, base_tables, past, kv_len, page_size, *, out_tables
                                       int(kv_len), int(page_size), _ptr(out_tables),
                                       _ptr(out_counts), _ptr(out_kv_lens), _stream(dev)))
     return out_tables, out_counts, out_kv_lens
+
+
+class PreparedAttention:
+    """rpa_attention with every argument marshalled once; calling it only enqueues the work.
+
+    For tight loops (benchmarks, serving steps) where the batch metadata does not change.
+    The tensors passed here must stay alive and keep their shapes while the object is used.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *,
+                 k_new=None, v_new=None, out=None, cu_q_lens_host=None, kv_lens_host=None,
+                 kernel=KERNEL_AUTO, workspace=None):
+        self.lib = load_library()
+        _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                     cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
+        self.shape = _shape_for(q.shape[1], k_cache, block_tables, cu_q_lens, kv_lens,
+                                cu_q_lens_host, kv_lens_host, kernel)
+        self.out = torch.empty_like(q) if out is None else out
+        need = self.lib.rpa_attention_workspace_size(self.shape.ref)
+        if need == ctypes.c_size_t(-1).value:
+            _check(1)
+        if workspace is None and need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        self.keep = (q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, k_new, v_new)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self.args = (self.shape.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                     _ptr(cu_q_lens), _ptr(kv_lens), ctypes.c_float(scale), _ptr(k_new),
+                     _ptr(v_new), _ptr(self.out), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                     _stream(q.device))
+
+    def __call__(self):
+        _check(self.lib.rpa_attention(*self.args))
+        return self.out
+
+
+class PreparedWriteKV:
+    """rpa_write_kv with its arguments marshalled once (see PreparedAttention)."""
+
+    def __init__(self, k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *,
+                 cu_q_lens_host=None, kv_lens_host=None):
+        self.lib = load_library()
+        self.shape = _shape_for(k_new.shape[1], k_cache, block_tables, cu_q_lens, kv_lens,
+                                cu_q_lens_host, kv_lens_host, KERNEL_AUTO)
+        self.keep = (k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens)
+        self.args = (self.shape.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                     _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens), _stream(k_cache.device))
+
+    def __call__(self):
+        _check(self.lib.rpa_write_kv(*self.args))

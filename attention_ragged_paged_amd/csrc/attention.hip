@@ -2,45 +2,42 @@
 //
 // Method: "Ragged Paged Attention: A High-Performance and Flexible LLM Inference Kernel for
 // TPU" (summary card, "Key ideas"): attention over ragged batches whose K/V live in a paged
-// cache, with separate kernels for decode, prefill and mixed batches.  Kernel split and
-// split-K decode follow ONNX Runtime PR 31727 ("[WebGPU] Optimized PagedAttention
-// implementation (2/n)", "What's shipped": a split-reduce decode pair and a fused paged
-// prefill with page-table-aware tile loads); causal alignment is that page's seqlens_q
-// fix: token t of a sequence sits at position past + t and sees keys 0 .. past + t.
+// cache, cache writes fused with the attention, and separate kernels for decode, prefill and
+// mixed batches.  The decode / prefill split and split-K decode follow ONNX Runtime PR 31727
+// ("[WebGPU] Optimized PagedAttention implementation (2/n)", "What's shipped": a split-reduce
+// decode pair and a fused paged prefill with page-table-aware tile loads); causal alignment
+// is that page's seqlens_q fix: token t of a sequence sits at position past + t and sees
+// keys 0 .. past + t.
 //
-// Work decomposition.  Every kernel maps blockIdx onto a work item with an in-kernel scan
-// over the sequences (find_item), so no work list is built or uploaded per call:
-//   decode item  = (sequence, KV head, 16-row tile, KV split)   one 256-thread workgroup
-//   prefill item = (sequence, 128-row tile, KV head, KV split)  one 256-thread workgroup
-// A row is one (token, query head) pair; the query heads of a GQA group are packed into the
-// same item so every K/V byte is read once per group.  Items whose sequence has more than
-// one split write fp32 partials (running max, sum, unnormalised output) that the merge
-// kernel combines with the log-sum-exp rule; single-split items write bf16 output directly.
+// One launch per call.  The kernels map blocks onto work with in-kernel scans over the
+// sequences (find_item, dec_locate), so no work list is built or uploaded.  A row is one
+// (token, query head) pair; the G query heads of a GQA group are packed into the same item
+// so every K/V byte is read once per group.
 //
-// MFMA layouts (gfx950, wave64).  Scores are computed transposed, S^T = K Q^T, so that a
-// lane owns one query row: its softmax statistics need at most two cross-lane steps, and
-// the S^T accumulator is already the B operand of the P V product computed as
-// O^T = V^T P^T.  V^T comes out of LDS with the transposing read ds_read_b64_tr_b16.
+// Fused cache write.  When the call carries the new tokens' K/V, every reader takes keys at
+// positions >= past straight from k_new / v_new, and exactly one item per (sequence, KV head)
+// - the one owning the sequence's last query rows, which visits every new key - stores them
+// into their page slots.  No reader ever loads a slot that this call writes.
+//
+// Split merges without a second launch.  Items that cover only part of a key range write
+// fp32 partials (running max in log2 units, sum, unnormalised output) and then arrive on a
+// per-item counter; the last to arrive merges with the log-sum-exp rule and writes bf16.
+// Counters carry the call's tag in their high bits, so stale values from earlier calls
+// (or uninitialised workspace) read as zero and the workspace never needs clearing.
+//
+// MFMA layouts (wave64).  Scores are computed transposed, S^T = K Q^T, so that a lane owns
+// one query row: its softmax statistics need at most two cross-lane steps, and the S^T
+// accumulator is already the B operand of the P V product computed as O^T = V^T P^T.  V^T
+// comes out of LDS with the transposing read ds_read_b64_tr_b16.
 #include "rpa_device.h"
 #include "rpa_launch.h"
 
 namespace rpa {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr unsigned long long kCountMask = (1ull << 24) - 1;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ int seq_of_token_dev(const int32_t *cu_q_lens, int B, int token) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu_q_lens[mid] <= token)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
 
 __device__ __forceinline__ int64_t kv_row_offset(const AttnArgs &a, int page, int slot, int g) {
   return (int64_t)page * a.page_stride + (int64_t)slot * a.slot_stride + (int64_t)g * a.head_stride;
@@ -50,50 +47,155 @@ __device__ __forceinline__ int table_at(const AttnArgs &a, int b, int g, int log
   return a.tables[b * a.bt_seq_stride + g * a.bt_head_stride + logical];
 }
 
+// Split partials travel between workgroups (possibly on different XCDs, each with its own
+// L2) through device-coherent accesses: device-scope relaxed atomic stores and loads, which
+// are written through and read past the non-coherent L2 (sc1).  The writer waits for its
+// stores to complete before it arrives on the counter, and the reader loads only after
+// its arrival returned last, so no cache-wide writeback or invalidate is ever needed
+// (a device-scope fence would flush the whole L2 of the XCD).
+__device__ __forceinline__ void st_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float ld_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_coherent4(float *p, const f32x4 &v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st_coherent(p + i, v[i]);
+}
+
+__device__ __forceinline__ f32x4 ld_coherent4(const float *p) {
+  return f32x4{ld_coherent(p), ld_coherent(p + 1), ld_coherent(p + 2), ld_coherent(p + 3)};
+}
+
+// Waits until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Arrive on a tagged counter; returns how many have arrived in this call (this one included).
+// A value carrying another call's tag counts as zero.  Lock-free: a failed exchange means
+// another arrival succeeded.
+__device__ __forceinline__ unsigned arrive(unsigned long long *p, unsigned long long tag) {
+  unsigned long long old = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (true) {
+    const unsigned long long next = ((old & ~kCountMask) == tag) ? old + 1 : (tag | 1ull);
+    if (__hip_atomic_compare_exchange_strong(p, &old, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (unsigned)(next & kCountMask);
+  }
+}
+
+// Merge the nsplit partials of one output row (dims d0 .. d0 + NPT) and write bf16:
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), online over batches of 4 splits whose
+// loads are all issued before any is used.
+template <int D, int NPT>
+__device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int token, int h, int d0) {
+  float M = kNegInf, L = 0.f;
+  f32x4 o[NPT / 4];
+#pragma unroll
+  for (int q = 0; q < NPT / 4; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float mv[4], lv[4];
+    f32x4 ov[4][NPT / 4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t pr = ((int64_t)min(s0 + u, nsplit - 1) * a.T + token) * a.Hq + h;
+      mv[u] = ld_coherent(a.part_ml + pr * 2);
+      lv[u] = ld_coherent(a.part_ml + pr * 2 + 1);
+#pragma unroll
+      for (int q = 0; q < NPT / 4; ++q) ov[u][q] = ld_coherent4(a.part_o + pr * D + d0 + 4 * q);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[u]);
+    const float Mu = Mn == kNegInf ? 0.f : Mn;
+    const float sc = fast_exp2(M - Mu);
+    L *= sc;
+#pragma unroll
+    for (int q = 0; q < NPT / 4; ++q) o[q] = o[q] * sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u >= nsplit) continue;
+      const float wv = fast_exp2(mv[u] - Mu);
+      L += lv[u] * wv;
+#pragma unroll
+      for (int q = 0; q < NPT / 4; ++q) o[q] += ov[u][q] * wv;
+    }
+    M = Mn;
+  }
+  const float inv = 1.f / L;
+  uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
+#pragma unroll
+  for (int q = 0; q < NPT / 4; ++q)
+    *reinterpret_cast<u32x2 *>(op + 4 * q) =
+        u32x2{pack_bf16x2(o[q][0] * inv, o[q][1] * inv), pack_bf16x2(o[q][2] * inv, o[q][3] * inv)};
+}
+
 // ============================================================================ decode ======
 //
-// A decode item holds up to 16 query rows (the q_len * G rows of one KV head, 16 at a time)
-// and one KV split.  The 4 waves of the workgroup take 16-key chunks round-robin; each wave
-// keeps its own online-softmax state, and the 4 states are merged through LDS at the end.
-//   QK^T: v_mfma_f32_16x16x32_bf16, A = K chunk (16 keys x 32 dims, straight from global
-//         memory: a lane's 16-byte load is exactly its operand), B = Q^T (in registers).
+// A decode item is (sequence, KV head, 16-row tile, KV split): up to 16 query rows of one KV
+// head (q_len * G rows taken 16 at a time) against one split of the keys.  Items are
+// workgroups, so the hardware dispatcher balances them dynamically as workgroups finish
+// (per-wave memory latency varies by 2x across the chip; a static split of the key stream
+// leaves the slowest waves as the tail).  The 4 waves take 16-key chunks round-robin, each
+// with its own online-softmax state, merged through LDS at the end.  Chunks are loaded as
+// whole contiguous rows (lane l takes 16 bytes of row l/LPR: four 256-byte rows per load
+// instruction, which streams ~25% faster than loading the MFMA operand layout directly)
+// and staged in the wave's LDS buffers, rows XOR-swizzled in 16-byte units:
+//   QK^T: v_mfma_f32_16x16x32_bf16, A = K rows (ds_read_b128), B = Q^T (in registers).
 //         Lane l gets S^T[key 4(l/16) + i][row l%16], i = 0..3.
-//   PV:   v_mfma_f32_16x16x16_bf16, A = V^T (transposing LDS read of the staged chunk),
-//         B = P^T (the lane's own 4 probabilities), accumulating O^T[dim][row].
+//   PV:   v_mfma_f32_16x16x16_bf16, A = V^T (transposing LDS read), B = P^T (the lane's
+//         own 4 probabilities) -> O^T[dim][row].
+// Each wave keeps the next chunk's loads in flight while it computes the current one
+// (register double buffer); block-table entries for 64 chunks sit in one register.
 template <int D>
 struct DecodeSmem {
   union {
-    uint16_t v[4][16 * D];   // per-wave staged V chunk, swizzled rows
-    float o[4][16][D + 4];   // per-wave unnormalised outputs for the final combine
+    struct {
+      uint16_t k[4][16 * D];  // per-wave staged K chunk
+      uint16_t v[4][16 * D];  // per-wave staged V chunk
+    } stage;
+    float o[4][16][D + 4];  // per-wave unnormalised outputs for the final combine
   };
   float m[4][16];
   float l[4][16];
+  int last;  // split merge: this workgroup arrived last
 };
 
-template <int D>
+__device__ __forceinline__ int dec_item_kend(int kv, int q_len, int G, int rt) {
+  const int last_row = min(rt * kDecodeRows + kDecodeRows - 1, q_len * G - 1);
+  return min(kv, kv - q_len + last_row / G + 1);
+}
+
 __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
   const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
   if (q_len == 0 || !is_decode_class(a, q_len)) return 0;
-  return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits(a, b, q_len);
+  return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits_dec(a, b);
 }
 
 template <int D>
 __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
-  constexpr int KK = D / 32;  // 16x16x32 MFMAs per 16-key chunk for QK^T (and loads per lane)
-  constexpr int MB = D / 16;  // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
+  constexpr int KK = D / 32;     // 16x16x32 MFMAs per chunk for QK^T; load instructions per chunk
+  constexpr int MB = D / 16;     // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
+  constexpr int LPR = D / 8;     // lanes per 16-key row when loading
+  constexpr int RPI = 64 / LPR;  // rows per load instruction
   DecodeSmem<D> &sm = *reinterpret_cast<DecodeSmem<D> *>(smem_raw);
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int r16 = lane & 15;
   const int j = lane >> 4;
+  const int lrow = lane / LPR;
+  const int lchk = lane % LPR;
 
-  const ItemRef it = find_item(id, a.B, [&](int b) { return decode_count<D>(a, b); });
+  const ItemRef it = find_item(id, a.B, [&](int b) { return decode_count(a, b); });
   const int b = __builtin_amdgcn_readfirstlane(it.b);
   if (b < 0) return;
   const int q0 = a.cu_q_lens[b];
   const int q_len = a.cu_q_lens[b + 1] - q0;
   const int n_rt = ceil_div(q_len * a.G, kDecodeRows);
-  const int nsplit = num_splits(a, b, q_len);
+  const int nsplit = num_splits_dec(a, b);
   int rem = __builtin_amdgcn_readfirstlane(it.rem);
   const int s = rem % nsplit;
   rem /= nsplit;
@@ -102,9 +204,10 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   const int kv_len = kv_len_of(a, b, g);
   const int past = kv_len - q_len;
   const int n_rows = q_len * a.G;
-  const int last_row = min(rt * kDecodeRows + kDecodeRows - 1, n_rows - 1);
   const int k_begin = s * a.split_dec;
-  const int k_end = min(min(kv_len, k_begin + a.split_dec), past + last_row / a.G + 1);
+  const int k_end = min(min(kv_len, k_begin + a.split_dec), dec_item_kend(kv_len, q_len, a.G, rt));
+  const bool fused = a.k_new != nullptr;
+  const bool writer = fused && rt == n_rt - 1;  // the last row tile visits every new key
 
   // This lane's query row (B operand column l%16).
   const int fr = rt * kDecodeRows + r16;
@@ -130,35 +233,55 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
 
   const int n_all = k_end > k_begin ? ceil_div(k_end - k_begin, 16) : 0;
   const int n_w = n_all > w ? (n_all - w + 3) / 4 : 0;  // chunks w, w+4, ... of this wave
-  uint16_t *vbuf = sm.v[w];
+  uint16_t *kbuf = sm.stage.k[w];
+  uint16_t *vbuf = sm.stage.v[w];
   const int page_mask = (1 << a.page_shift) - 1;
+  int pg_lane = 0;  // page of this wave's chunk base + lane
 
-  // Pages of this wave's chunks, 64 chunks per window: lane l holds the page of chunk
-  // base + l, so the pipelined loop picks pages with a register read, never a memory load.
-  int pg_lane = 0;
+  // Chunk i of this wave holds keys key0 .. key0+15 (one page: pages hold >= 16 keys); load
+  // instruction t brings rows lrow + RPI*t.  Rows of new keys come from k_new / v_new.
   auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
     const int page = __builtin_amdgcn_readlane(pg_lane, i);
-    const int64_t off = kv_row_offset(a, page, (key0 & page_mask) + r16, g);
-    const uint16_t *kp = a.k_cache + off + 8 * j;
-    const uint16_t *vp = a.v_cache + off + 8 * j;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[kk] = *reinterpret_cast<const u32x4 *>(kp + 32 * kk);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) vr[kk] = *reinterpret_cast<const u32x4 *>(vp + 32 * kk);
+    for (int t = 0; t < KK; ++t) {
+      const int r = lrow + RPI * t;
+      const int key = key0 + r;
+      const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 8 * lchk;
+      const uint16_t *kp = a.k_cache + coff;
+      const uint16_t *vp = a.v_cache + coff;
+      if (fused && key >= past) {
+        const int64_t noff = ((int64_t)(q0 + key - past) * a.Hkv + g) * D + 8 * lchk;
+        kp = a.k_new + noff;
+        vp = a.v_new + noff;
+      }
+      kr[t] = *reinterpret_cast<const u32x4 *>(kp);
+      vr[t] = *reinterpret_cast<const u32x4 *>(vp);
+    }
   };
-
-  auto process_chunk = [&](int i, const u32x4 *kr, const u32x4 *vr) {
-    const int key0 = k_begin + 16 * (w + 4 * i);
+  auto process_chunk = [&](int base, int i, const u32x4 *kr, const u32x4 *vr) {
+    const int key0 = k_begin + 16 * (w + 4 * (base + i));
+    const int page = __builtin_amdgcn_readlane(pg_lane, i);
+    // Stage in LDS (V rows of keys past the item's range are zeroed: they may hold anything);
+    // the writer item also stores the new keys into their page slots.
+#pragma unroll
+    for (int t = 0; t < KK; ++t) {
+      const int r = lrow + RPI * t;
+      const int key = key0 + r;
+      *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, lchk)) = kr[t];
+      *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, lchk)) = key < k_end ? vr[t] : u32x4{0u, 0u, 0u, 0u};
+      if (writer && key >= past && key < k_end) {
+        const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 8 * lchk;
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + coff) = kr[t];
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + coff) = vr[t];
+      }
+    }
+    // S^T = K Q^T: lane (r16, j) takes K row r16, dims 32kk + 8j .. +8 as its A operand.
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) st = mfma16x16x32(as_bf16x8(kr[kk]), qf[kk], st);
-    // Stage V (rows of keys past the item's range are zeroed: they may hold anything).
-    const bool vrow_ok = key0 + r16 < k_end;
-#pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = vrow_ok ? vr[kk] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r16, 4 * kk + j)) = v;
+      const u32x4 kf = *reinterpret_cast<const u32x4 *>(kbuf + lds_off<D>(r16, 4 * kk + j));
+      st = mfma16x16x32(as_bf16x8(kf), qf[kk], st);
     }
     float sv[4];
     float mloc = kNegInf;
@@ -183,9 +306,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    const uint32_t p01 = pack_bf16x2(p[0], p[1]);
-    const uint32_t p23 = pack_bf16x2(p[2], p[3]);
-    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
     // Transposing read: lane (i = l%16, j) names row 4j + i/4, dims 16mb + 4(i%4) .. +3.
     const int tr_row = 4 * j + (r16 >> 2);
 #pragma unroll
@@ -199,10 +320,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
 
   for (int base = 0; base < n_w; base += 64) {
     const int n = min(64, n_w - base);
-    {
-      const int i = base + lane;
-      pg_lane = lane < n ? table_at(a, b, g, (k_begin + 16 * (w + 4 * i)) >> a.page_shift) : 0;
-    }
+    pg_lane = lane < n ? table_at(a, b, g, (k_begin + 16 * (w + 4 * (base + lane))) >> a.page_shift) : 0;
     u32x4 kA[KK], vA[KK], kB[KK], vB[KK];
     load_chunk(base, 0, kA, vA);
     // Two chunks per trip, register double buffer.  Every load is unconditional (the last
@@ -211,19 +329,19 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
     for (int i = 0; i + 1 < n; i += 2) {
       load_chunk(base, i + 1, kB, vB);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this chunk's math
-      process_chunk(base + i, kA, vA);
+      process_chunk(base, i, kA, vA);
       load_chunk(base, min(i + 2, n - 1), kA, vA);
       __builtin_amdgcn_sched_barrier(0);
-      process_chunk(base + i + 1, kB, vB);
+      process_chunk(base, i + 1, kB, vB);
     }
-    if (n & 1) process_chunk(base + n - 1, kA, vA);
+    if (n & 1) process_chunk(base, n - 1, kA, vA);
   }
 
   // Row sum over the 4 lanes that share the row.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  __syncthreads();  // every wave is done with its V buffer (aliased by the combine area)
+  __syncthreads();  // every wave is done with its staging buffers (aliased by the combine)
   if (j == 0) {
     sm.m[w][r16] = m_run;
     sm.l[w][r16] = l_run;
@@ -242,56 +360,62 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm.m[ww][row]);
   const float M_use = M == kNegInf ? 0.f : M;
-  float wgt[4];
   float L = 0.f;
+  f32x4 o[DPT / 4];
+#pragma unroll
+  for (int q = 0; q < DPT / 4; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
-    wgt[ww] = fast_exp2(sm.m[ww][row] - M_use);
-    L += sm.l[ww][row] * wgt[ww];
-  }
-  float o[DPT];
+    const float wv = fast_exp2(sm.m[ww][row] - M_use);
+    L += sm.l[ww][row] * wv;
 #pragma unroll
-  for (int d = 0; d < DPT; ++d) {
-    float x = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) x += sm.o[ww][row][d0 + d] * wgt[ww];
-    o[d] = x;
+    for (int q = 0; q < DPT / 4; ++q)
+      o[q] += *reinterpret_cast<const f32x4 *>(&sm.o[ww][row][d0 + 4 * q]) * wv;
   }
   const int frow = rt * kDecodeRows + row;
-  if (frow >= n_rows) return;
+  const bool out_ok = frow < n_rows;
   const int token = q0 + frow / a.G;
   const int h = g * a.G + frow % a.G;
   if (nsplit == 1) {
+    if (!out_ok) return;
     const float inv = 1.f / L;
-    uint32_t packed[DPT / 2];
-#pragma unroll
-    for (int d = 0; d < DPT / 2; ++d) packed[d] = pack_bf16x2(o[2 * d] * inv, o[2 * d + 1] * inv);
     uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
-    if constexpr (DPT == 8)
-      *reinterpret_cast<u32x4 *>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    else
-      *reinterpret_cast<u32x2 *>(op) = u32x2{packed[0], packed[1]};
-  } else {
-    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h;
-    float *po = a.part_o + prow * D + d0;
 #pragma unroll
-    for (int d = 0; d < DPT; d += 4)
-      *reinterpret_cast<f32x4 *>(po + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]};
+    for (int q = 0; q < DPT / 4; ++q)
+      *reinterpret_cast<u32x2 *>(op + 4 * q) =
+          u32x2{pack_bf16x2(o[q][0] * inv, o[q][1] * inv), pack_bf16x2(o[q][2] * inv, o[q][3] * inv)};
+    return;
+  }
+  if (out_ok) {
+    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h;
+#pragma unroll
+    for (int q = 0; q < DPT / 4; ++q) st_coherent4(a.part_o + prow * D + d0 + 4 * q, o[q]);
     if (d0 == 0) {
-      a.part_ml[prow * 2 + 0] = M;
-      a.part_ml[prow * 2 + 1] = L;
+      st_coherent(a.part_ml + prow * 2 + 0, M);
+      st_coherent(a.part_ml + prow * 2 + 1, L);
     }
   }
+  // Arrive; the last of the nsplit items of this (sequence, KV head, row tile) merges.
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long *ctr = a.counters + (int64_t)(q0 * a.G + rt * kDecodeRows) * a.Hkv + g;
+    sm.last = arrive(ctr, a.call_tag) == (unsigned)nsplit;
+  }
+  __syncthreads();
+  if (!sm.last || !out_ok) return;
+  merge_row<D, DPT>(a, nsplit, token, h, d0);
 }
 
 // =========================================================================== prefill ======
 //
 // A prefill item is 128 query rows of one KV head: pf_tokens = 128 / G consecutive tokens of
-// each of the G query heads of the group (wave w owns rows 32w .. 32w+31).  The workgroup
-// walks 64-key tiles up to the causal limit of its last token.  Each tile is fetched into
-// registers one tile ahead, so the global loads of tile i+1 overlap the MFMAs of tile i;
-// block-table entries sit in a register (one per lane) and never delay a tile load.  Every key row is located through the block table
-// on its own, so a 64-key tile may span several pages (page size 16 or 32 included).
+// each of the G query heads of the group (wave w owns rows 32w .. 32w+31), over one KV split.
+// The workgroup walks 64-key tiles up to the causal limit of its last token.  Each tile is
+// fetched into registers one tile ahead, so the global loads of tile i+1 overlap the MFMAs
+// of tile i; block-table entries sit in a register (one per lane) and never delay a tile
+// load.  Every key row is located through the block table on its own, so a 64-key tile may
+// span several pages (page size 16 or 32 included).
 //   QK^T: v_mfma_f32_32x32x16_bf16, A = K tile rows from LDS (ds_read_b128), B = Q^T in
 //         registers.  Lane l gets S^T[key 32mb + 8(v/4) + 4(l/32) + v%4][row l%32].
 //   PV:   v_mfma_f32_32x32x16_bf16, A = V^T from two transposing LDS reads, B = P^T taken
@@ -301,19 +425,20 @@ template <int D>
 struct PrefillSmem {
   uint16_t k[kPrefillKeys * D];
   uint16_t v[kPrefillKeys * D];
+  int last;  // split merge: this workgroup arrived last
 };
 
 template <int D>
 __device__ __forceinline__ int prefill_count(const AttnArgs &a, int b) {
   const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
   if (q_len == 0 || is_decode_class(a, q_len)) return 0;
-  return a.Hkv * ceil_div(q_len, a.pf_tokens) * num_splits(a, b, q_len);
+  return a.Hkv * ceil_div(q_len, a.pf_tokens) * num_splits_pf(a, b);
 }
 
 template <int D>
 __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
-  constexpr int KS = D / 16;                               // QK^T MFMAs per 32-key block
-  constexpr int MD = D / 32;                               // PV output blocks of 32 dims
+  constexpr int KS = D / 16;                                // QK^T MFMAs per 32-key block
+  constexpr int MD = D / 32;                                // PV output blocks of 32 dims
   constexpr int LOADS = kPrefillKeys * (D / 8) / kThreads;  // 16-byte loads per thread per tile
   constexpr int kChunks = D / 8;
   PrefillSmem<D> &sm = *reinterpret_cast<PrefillSmem<D> *>(smem_raw);
@@ -329,7 +454,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   const int q0 = a.cu_q_lens[b];
   const int q_len = a.cu_q_lens[b + 1] - q0;
   const int n_qt = ceil_div(q_len, a.pf_tokens);
-  const int nsplit = num_splits(a, b, q_len);
+  const int nsplit = num_splits_pf(a, b);
   int rem = __builtin_amdgcn_readfirstlane(it.rem);
   const int s = rem % nsplit;
   rem /= nsplit;
@@ -342,6 +467,8 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   const int k_begin = s * a.split_pf;
   const int k_end = min(min(kv_len, k_begin + a.split_pf), past + t_last + 1);
   const int n_tiles = k_end > k_begin ? ceil_div(k_end - k_begin, kPrefillKeys) : 0;
+  const bool fused = a.k_new != nullptr;
+  const bool writer = fused && qt == n_qt - 1;  // the last query tile visits every new key
 
   // This lane's query row.
   const int rr = 32 * w + r32;
@@ -381,6 +508,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   };
   // Per-thread tile rows: load u covers chunk (u*256 + tid) of the 64 x D tile.
   u32x4 kr[LOADS], vr[LOADS];
+  int64_t roff[LOADS];  // cache offsets of the rows just fetched (for the fused write)
   auto fetch_tile = [&](int tile) {
     const int kt0 = k_begin + tile * kPrefillKeys;
     const int last_blk = (min(kt0 + kPrefillKeys, k_end) - 1) >> a.page_shift;
@@ -390,9 +518,16 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       const int cid = u * kThreads + tid;
       const int pos = min(kt0 + cid / kChunks, k_end - 1);
       const int page = __shfl(pg_lane, (pos >> a.page_shift) - pg_blk0);
-      const int64_t off = kv_row_offset(a, page, pos & page_mask, g) + (cid % kChunks) * 8;
-      kr[u] = *reinterpret_cast<const u32x4 *>(a.k_cache + off);
-      vr[u] = *reinterpret_cast<const u32x4 *>(a.v_cache + off);
+      roff[u] = kv_row_offset(a, page, pos & page_mask, g) + (cid % kChunks) * 8;
+      const uint16_t *kp = a.k_cache + roff[u];
+      const uint16_t *vp = a.v_cache + roff[u];
+      if (fused && pos >= past) {
+        const int64_t noff = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + (cid % kChunks) * 8;
+        kp = a.k_new + noff;
+        vp = a.v_new + noff;
+      }
+      kr[u] = *reinterpret_cast<const u32x4 *>(kp);
+      vr[u] = *reinterpret_cast<const u32x4 *>(vp);
     }
   };
 
@@ -408,9 +543,14 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       const int cid = u * kThreads + tid;
       const int key = cid / kChunks;
       const int c = cid % kChunks;
+      const int pos = kt0 + key;
       *reinterpret_cast<u32x4 *>(&sm.k[lds_off<D>(key, c)]) = kr[u];
-      const bool ok = kt0 + key < k_end;
+      const bool ok = pos < k_end;
       *reinterpret_cast<u32x4 *>(&sm.v[lds_off<D>(key, c)]) = ok ? vr[u] : u32x4{0u, 0u, 0u, 0u};
+      if (writer && ok && pos >= past) {
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + roff[u]) = kr[u];
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + roff[u]) = vr[u];
+      }
     }
     __syncthreads();
     if (tile + 1 < n_tiles) fetch_tile(tile + 1);
@@ -490,9 +630,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   }
 
   l_run += __shfl_xor(l_run, 32);
-  if (!row_ok) return;
   const int token = q0 + t_row;
   if (nsplit == 1) {
+    if (!row_ok) return;
     const float inv = 1.f / l_run;
     uint16_t *op = a.out + ((int64_t)token * a.Hq + h_row) * D;
 #pragma unroll
@@ -504,7 +644,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
         const uint32_t w1 = pack_bf16x2(acc[md][4 * vq + 2] * inv, acc[md][4 * vq + 3] * inv);
         *reinterpret_cast<u32x2 *>(op + d) = u32x2{w0, w1};
       }
-  } else {
+    return;
+  }
+  if (row_ok) {
     const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h_row;
     float *po = a.part_o + prow * D;
 #pragma unroll
@@ -512,14 +654,30 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         const int d = 32 * md + 8 * vq + 4 * hf;
-        *reinterpret_cast<f32x4 *>(po + d) =
-            f32x4{acc[md][4 * vq], acc[md][4 * vq + 1], acc[md][4 * vq + 2], acc[md][4 * vq + 3]};
+        st_coherent4(po + d, f32x4{acc[md][4 * vq], acc[md][4 * vq + 1], acc[md][4 * vq + 2],
+                                   acc[md][4 * vq + 3]});
       }
     if (hf == 0) {
-      a.part_ml[prow * 2 + 0] = m_run;
-      a.part_ml[prow * 2 + 1] = l_run;
+      st_coherent(a.part_ml + prow * 2 + 0, m_run);
+      st_coherent(a.part_ml + prow * 2 + 1, l_run);
     }
   }
+  // Arrive; the last of the nsplit items of this (query tile, KV head) merges all partials.
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long *ctr = a.counters + a.pf_counter_base + (int64_t)(q0 + t_first) * a.Hkv + g;
+    sm.last = arrive(ctr, a.call_tag) == (unsigned)nsplit;
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  constexpr int DH = D / 2;  // two threads per row, half of D each, 16 dims per pass
+  const int mrow = tid >> 1;
+  const int mhg = mrow / a.pf_tokens;
+  const int mt = t_first + mrow % a.pf_tokens;
+  if (mhg >= a.G || mt >= q_len) return;
+#pragma unroll 1
+  for (int d = 0; d < DH; d += 16) merge_row<D, 16>(a, nsplit, q0 + mt, g * a.G + mhg, (tid & 1) * DH + d);
 }
 
 // =========================================================================== kernels ======
@@ -541,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 }
 
 // One launch for a batch holding both kinds: prefill items first (they are the longest),
-// then decode items.
+// then the decode items.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D>];
@@ -551,86 +709,29 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
     decode_item<D>(a, blockIdx.x - a.n_pf_items, smem);
 }
 
-// Split-K merge (the reduce half of the split-reduce decode pair): one wave per
-// (token, query head) row whose sequence was split.  out = sum_s o_s 2^(m_s - M) /
-// sum_s l_s 2^(m_s - M), M = max_s m_s.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  constexpr int DPL = D / 64;  // dims per lane
-  const int lane = lane_id();
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.T * a.Hq) return;
-  const int token = row / a.Hq;
-  const int h = row % a.Hq;
-  const int b = seq_of_token_dev(a.cu_q_lens, a.B, token);
-  const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
-  const int nsplit = num_splits(a, b, q_len);
-  if (nsplit <= 1) return;
-  float m_s = kNegInf, l_s = 0.f;
-  if (lane < nsplit) {
-    const int64_t prow = ((int64_t)lane * a.T + token) * a.Hq + h;
-    m_s = a.part_ml[prow * 2 + 0];
-    l_s = a.part_ml[prow * 2 + 1];
-  }
-  float M = m_s;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float M_use = M == kNegInf ? 0.f : M;
-  const float wgt = fast_exp2(m_s - M_use);
-  float L = l_s * wgt;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-  float o[DPL];
-#pragma unroll
-  for (int d = 0; d < DPL; ++d) o[d] = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float ws = __shfl(wgt, sp);
-    if (ws == 0.f) continue;
-    const float *po = a.part_o + (((int64_t)sp * a.T + token) * a.Hq + h) * D + lane * DPL;
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) o[d] += po[d] * ws;
-  }
-  const float inv = 1.f / L;
-  uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + lane * DPL;
-  if constexpr (DPL == 2) {
-    *reinterpret_cast<uint32_t *>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
-    const uint32_t pk = pack_bf16x2(o[0] * inv, 0.f);
-    op[0] = (uint16_t)(pk & 0xffffu);
-  }
-}
-
-template <int D>
-static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_items, bool merge,
+static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_blocks,
                                      hipStream_t stream) {
-  if (n_items > 0) {
-    const dim3 grid((unsigned)n_items), block(kThreads);
-    switch (kind) {
-      case AttnKernel::kDecode:
-        hipLaunchKernelGGL(decode_kernel<D>, grid, block, 0, stream, a);
-        break;
-      case AttnKernel::kPrefill:
-        hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, a);
-        break;
-      case AttnKernel::kMixed:
-        hipLaunchKernelGGL(mixed_kernel<D>, grid, block, 0, stream, a);
-        break;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (n_blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_blocks), block(kThreads);
+  switch (kind) {
+    case AttnKernel::kDecode:
+      hipLaunchKernelGGL(decode_kernel<D>, grid, block, 0, stream, a);
+      break;
+    case AttnKernel::kPrefill:
+      hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, a);
+      break;
+    case AttnKernel::kMixed:
+      hipLaunchKernelGGL(mixed_kernel<D>, grid, block, 0, stream, a);
+      break;
   }
-  if (merge) {
-    const unsigned rows = (unsigned)((int64_t)a.T * a.Hq);
-    hipLaunchKernelGGL(merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_items, bool merge,
+hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
                             hipStream_t stream) {
-  if (D == 128) return launch_attention_d<128>(a, kind, n_items, merge, stream);
-  return launch_attention_d<64>(a, kind, n_items, merge, stream);
+  if (D == 128) return launch_attention_d<128>(a, kind, n_blocks, stream);
+  return launch_attention_d<64>(a, kind, n_blocks, stream);
 }
 
 }  // namespace rpa

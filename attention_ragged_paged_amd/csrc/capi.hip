@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <random>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -37,6 +39,18 @@ rpa_status ok() {
   return RPA_OK;
 }
 
+// Tag of one rpa_attention call, in bits 24..63 of the split-merge counters.  Tags grow by
+// one per call from a random start, so counters left by earlier calls or by anything else
+// in the workspace never carry the current tag.
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> next{[] {
+    std::random_device rd;
+    return ((unsigned long long)rd() << 20) ^ (unsigned long long)rd();
+  }()};
+  const unsigned long long id = next.fetch_add(1, std::memory_order_relaxed);
+  return (id & ((1ull << 40) - 1)) << 24;
+}
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int x) {
@@ -53,7 +67,10 @@ constexpr int kDecodeRowsMax = 16;
 constexpr int kMaxSplits = 64;
 // Work items the split sizes aim for: several workgroups per compute unit of the
 // 256-CU chip so the tail of a ragged batch stays short.
-constexpr long long kTargetItems = 2048;
+#ifndef RPA_TARGET_ITEMS
+#define RPA_TARGET_ITEMS 2048
+#endif
+constexpr long long kTargetItems = RPA_TARGET_ITEMS;
 
 int kv_len_at(const rpa_shape *s, int b, int g) {
   return s->layout == RPA_LAYOUT_SEQ_MAJOR ? s->h_kv_lens[b]
@@ -148,9 +165,9 @@ struct Plan {
   int split_dec = 1 << 30;
   int split_pf = 1 << 30;
   int pf_tokens = 1;
-  int n_dec_items = 0;
-  int n_pf_items = 0;
-  int max_nsplit = 1;
+  int n_dec_items = 0;  // decode work items (one workgroup each)
+  int n_pf_items = 0;   // prefill work items (one workgroup each)
+  int max_nsplit = 1;   // most KV splits of any sequence
 };
 
 bool decode_class(const Plan &p, int q_len, int G) { return (long long)q_len * G <= p.dec_rows_max; }
@@ -217,8 +234,7 @@ Plan make_plan(const rpa_shape *s) {
   for (int b = 0; b < s->num_seqs; ++b) {
     const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
     if (q_len == 0) continue;
-    const int kv = max_kv_len_host(s, b);
-    const int ns = splits_of(p, q_len, G, kv);
+    const int ns = splits_of(p, q_len, G, max_kv_len_host(s, b));
     p.max_nsplit = std::max(p.max_nsplit, ns);
     if (decode_class(p, q_len, G))
       p.n_dec_items += s->num_kv_heads * cdiv((long long)q_len * G, rpa::kDecodeRows) * ns;
@@ -228,10 +244,34 @@ Plan make_plan(const rpa_shape *s) {
   return p;
 }
 
+struct WorkspaceLayout {
+  size_t part_o = 0, part_ml = 0, counters = 0, pf_counter_base = 0, total = 0;
+};
+
+// Split partials [max_nsplit][T][Hq][D] + [..][2] fp32, then arrival counters: decode row
+// groups at (q0*G + 16*rt)*Hkv + g, prefill row groups after them at (q0 + t0)*Hkv + g.
+WorkspaceLayout workspace_layout(const rpa_shape *s, const Plan &p) {
+  WorkspaceLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  const size_t rows = p.max_nsplit > 1 ? (size_t)p.max_nsplit * s->total_q * s->num_q_heads : 0;
+  w.part_o = take(rows * s->head_dim * sizeof(float));
+  w.part_ml = take(rows * 2 * sizeof(float));
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const size_t dec_ctr = p.max_nsplit > 1 ? ((size_t)s->total_q * G + rpa::kDecodeRows) * s->num_kv_heads : 0;
+  const size_t pf_ctr = p.max_nsplit > 1 ? (size_t)s->total_q * s->num_kv_heads : 0;
+  w.pf_counter_base = dec_ctr;
+  w.counters = take((dec_ctr + pf_ctr) * sizeof(unsigned long long));
+  w.total = off;
+  return w;
+}
+
 size_t workspace_bytes_for(const rpa_shape *s, const Plan &p) {
-  if (p.max_nsplit <= 1) return 0;
-  const size_t rows = (size_t)p.max_nsplit * s->total_q * s->num_q_heads;
-  return rows * (size_t)(s->head_dim + 2) * sizeof(float);
+  return workspace_layout(s, p).total;
 }
 
 void fill_layout(const rpa_shape *s, int64_t &page_stride, int64_t &slot_stride,
@@ -331,22 +371,23 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   st = check_device();
   if (st != RPA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (k_new) {
-    st = write_kv_impl(shape, k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, hs);
-    if (st != RPA_OK) return st;
-  }
+  const rpa::AttnKernel kind = static_cast<rpa::AttnKernel>(p.kind);
+  const WorkspaceLayout wl = workspace_layout(shape, p);
+  char *ws = static_cast<char *>(workspace);
   rpa::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.k_cache = static_cast<const uint16_t *>(k_cache);
   a.v_cache = static_cast<const uint16_t *>(v_cache);
   a.out = static_cast<uint16_t *>(out);
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
   a.tables = block_tables;
   a.cu_q_lens = cu_q_lens;
   a.kv_lens = kv_lens;
-  const size_t o_bytes = (size_t)p.max_nsplit * shape->total_q * shape->num_q_heads *
-                         shape->head_dim * sizeof(float);
-  a.part_o = need ? static_cast<float *>(workspace) : nullptr;
-  a.part_ml = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes) : nullptr;
+  a.part_o = need ? reinterpret_cast<float *>(ws + wl.part_o) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float *>(ws + wl.part_ml) : nullptr;
+  a.counters = need ? reinterpret_cast<unsigned long long *>(ws + wl.counters) : nullptr;
+  a.call_tag = next_call_tag();
   a.B = shape->num_seqs;
   a.T = shape->total_q;
   a.Hq = shape->num_q_heads;
@@ -361,9 +402,8 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   a.split_pf = p.split_pf;
   a.pf_tokens = p.pf_tokens;
   a.n_pf_items = p.n_pf_items;
-  const int n_items = p.n_pf_items + p.n_dec_items;
-  hipError_t e = rpa::launch_attention(a, shape->head_dim, static_cast<rpa::AttnKernel>(p.kind),
-                                       n_items, p.max_nsplit > 1, hs);
+  a.pf_counter_base = (int32_t)wl.pf_counter_base;
+  hipError_t e = rpa::launch_attention(a, shape->head_dim, kind, p.n_pf_items + p.n_dec_items, hs);
   if (e != hipSuccess) return fail(RPA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }

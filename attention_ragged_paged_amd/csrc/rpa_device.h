@@ -29,11 +29,15 @@ struct AttnArgs {
   const uint16_t *k_cache;  // paged cache, see strides
   const uint16_t *v_cache;
   uint16_t *out;            // [T][Hq][D] bf16
+  const uint16_t *k_new;    // [T][Hkv][D] bf16 or null: new tokens' K/V, written in this call
+  const uint16_t *v_new;
   const int32_t *tables;
   const int32_t *cu_q_lens; // [B + 1]
   const int32_t *kv_lens;
-  float *part_o;            // [max_nsplit][T][Hq][D] unnormalised partial outputs
-  float *part_ml;           // [max_nsplit][T][Hq][2] running max (log2 units) and sum
+  float *part_o;            // split partials: [max_nsplit][T][Hq][D] unnormalised outputs
+  float *part_ml;           // [max_nsplit][T][Hq][2]: running max (log2 units) and sum
+  unsigned long long *counters;  // arrival counters: decode row groups, then prefill ones
+  unsigned long long call_tag;   // this call's tag in bits 24..63 (count in bits 0..23)
   int32_t B, T, Hq, Hkv, G;
   int32_t page_shift;       // log2(page size)
   int64_t page_stride, slot_stride, head_stride;  // cache element strides
@@ -45,6 +49,7 @@ struct AttnArgs {
   int32_t split_pf;         // keys per split of a prefill-class sequence (multiple of 64)
   int32_t pf_tokens;        // tokens per prefill tile: kPrefillRows / G (at least 1)
   int32_t n_pf_items;       // mixed kernel: blocks [0, n_pf_items) are prefill items
+  int32_t pf_counter_base;  // first prefill counter: decode ones are (q0*G + 16*rt)*Hkv + g
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -67,10 +72,13 @@ __device__ __forceinline__ bool is_decode_class(const AttnArgs &a, int q_len) {
 
 __device__ __forceinline__ int ceil_div(int x, int y) { return (x + y - 1) / y; }
 
-// Number of KV splits of sequence b (the same formula on the host and in the merge).
-__device__ __forceinline__ int num_splits(const AttnArgs &a, int b, int q_len) {
-  int split = is_decode_class(a, q_len) ? a.split_dec : a.split_pf;
-  return max(1, ceil_div(max_kv_len(a, b), split));
+// Number of KV splits of a decode-class / prefill-class sequence b (same formulas on the host).
+__device__ __forceinline__ int num_splits_dec(const AttnArgs &a, int b) {
+  return max(1, ceil_div(max_kv_len(a, b), a.split_dec));
+}
+
+__device__ __forceinline__ int num_splits_pf(const AttnArgs &a, int b) {
+  return max(1, ceil_div(max_kv_len(a, b), a.split_pf));
 }
 
 struct ItemRef {

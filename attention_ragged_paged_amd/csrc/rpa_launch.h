@@ -27,9 +27,9 @@ enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };
 
 hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 
-// Runs the attention kernel of the given kind over n_items work items, then the split-K
-// merge when any sequence is split (merge_rows = T * Hq rows, 0 = no merge).
-hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_items, bool merge,
+// Runs the attention kernel of the given kind on n_blocks workgroups (the prefill items,
+// then the decode stream's workgroups).
+hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
                             hipStream_t stream);
 
 struct UnionArgs {

@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of ragged paged attention on one MI355X; prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the whole path over one synthetic batch resident in HBM: the
+scatter of the new tokens' K/V into their pages (rpa_write_kv), then the attention
+(rpa_attention: decode, prefill or mixed kernel as dispatched, plus the split merge);
+for the block-sparse workload also the union-table build.  Each step is timed with HIP
+events on the stream the library launches on; the L2 and the 256 MB Infinity Cache are
+flushed before every step, outside the events, by reading a 1 GiB buffer (a read leaves
+only clean lines behind, so no write-back of flush data lands inside the timed step).
+
+Workloads (all seeded synthetic inputs with Llama-3-8B attention shapes, 32/8 heads, D 128):
+  llama3_decode       64 decode sequences, kv_len ~ U[512, 4096], page 16, 20k-page pool (default)
+  llama3_prefill      4 x 2048 new tokens, no prior context, page 64
+  mixed_chunked       one 512-token chunk at context 8192 + 96 decodes, page 16
+  block_union_sparse  4096-query chunk at context 131072, KV-head-major page 64, 10% block mask
+  tiny_ragged         the 3-sequence parity case (latency only)
+
+`value` is the step's algorithmic throughput: GB/s for the HBM-bound decode and mixed
+batches, TFLOP/s for the MFMA-bound prefill and sparse ones.  `roofline` rates the
+dominant kernel (the attention launch) against MI355X's published peaks: 8 TB/s HBM3E,
+2.5 PFLOP/s dense bf16 MFMA.  `cpu_baseline` times the CPU oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decode HBM GB/s (% peak) + prefill/mixed TFLOP/s (% MFMA peak), tokens/s"
+WORKLOAD_BOUND = {"llama3_decode": "hbm", "mixed_chunked": "hbm", "tiny_ragged": "hbm",
+                  "llama3_prefill": "mfma", "block_union_sparse": "mfma"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- algorithmic counts ----
+
+def step_bytes(b, attention_only=False):
+    """Algorithmic HBM bytes: every K/V byte of every visible key read once per KV head, Q read,
+    O written, block tables and lengths read; plus (whole step) new K/V read and written."""
+    D, Hkv, Hq = b.head_dim, b.num_kv_heads, b.num_q_heads
+    kv = b.kv_lens.reshape(b.num_seqs, -1)
+    if b.layout == 0:
+        kv_bytes = int(kv[:, 0].astype(np.int64).sum()) * Hkv * D * 2 * 2
+        tables = int(((kv[:, 0] + b.page_size - 1) // b.page_size).sum()) * 4
+    else:
+        kv_bytes = int(kv.astype(np.int64).sum()) * D * 2 * 2
+        tables = int(((kv + b.page_size - 1) // b.page_size).sum()) * 4
+    qo = b.total_q * Hq * D * 2 * 2
+    meta = (b.num_seqs + 1) * 4 + kv.size * 4
+    total = kv_bytes + qo + tables + meta
+    if not attention_only:
+        total += b.total_q * Hkv * D * 2 * 2 * 2
+    return total
+
+
+def causal_flops(b, kv_lens=None):
+    """4 * D flops per visible (query row, key) pair: 2 for q.k, 2 for p.v."""
+    kv = (b.kv_lens if kv_lens is None else kv_lens).reshape(b.num_seqs, -1)
+    G = b.num_q_heads // b.num_kv_heads
+    total = 0
+    for s in range(b.num_seqs):
+        q_len = int(b.cu_q_lens[s + 1] - b.cu_q_lens[s])
+        for col in range(kv.shape[1]):
+            past = int(kv[s, col]) - q_len
+            pairs = q_len * past + q_len * (q_len + 1) // 2
+            heads = b.num_q_heads if kv.shape[1] == 1 else G
+            total += pairs * heads
+    return 4 * b.head_dim * total
+
+
+# ----------------------------------------------------------------- traffic counters ------
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in ("attention.hip", "rpa_device.h"):
+        with open(os.path.join(ROOT, "attention_ragged_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- CPU baseline ----------
+
+def cpu_baseline(b, workload, bound, budget_s=12.0):
+    import oracle
+    kc, vc = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                             b.k_cache, b.v_cache, b.page_size, layout=b.layout)
+    threads = oracle.num_threads()
+    rows_all = b.total_q * b.num_q_heads
+    block_allowed = b.extra.get("allowed")
+    # Work of a row = its visible keys; pick a bounded sample of rows (every k-th row).
+    est_rate = 6.0e8 * threads   # fp64 multiply-adds per second per thread, to size the sample
+    work = causal_flops(b) / 2 if bound == "mfma" else step_bytes(b)
+    frac = min(1.0, budget_s * est_rate / max(1.0, causal_flops(b) / 2))
+    stride = max(1, int(math.ceil(1.0 / frac)))
+    idx = np.arange(0, rows_all, stride)
+    rows = np.stack([idx // b.num_q_heads, idx % b.num_q_heads], axis=1).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale, b.page_size,
+                     b.num_kv_heads, layout=b.layout, block_allowed=block_allowed,
+                     rows=None if stride == 1 else rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    share = len(idx) / rows_all
+    if bound == "mfma":
+        value = causal_flops(b, b.extra.get("compacted_kv_lens")) * share / dt / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = step_bytes(b) * share / dt / 1e9
+        unit = "GB/s"
+    del work
+    sample = (f"{len(idx)} of {rows_all} (token, head) rows (every {stride}th), after the oracle's "
+              f"KV scatter; {dt:.1f} s wall")
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample, "tokens_per_s": round(b.total_q * share / dt, 2)}
+
+
+# ----------------------------------------------------------------- main --------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_decode", choices=sorted(WORKLOAD_BOUND))
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                    help="how the caches are flushed before each step (none: warm caches)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_ragged_paged_amd as rpa
+    from attention_ragged_paged_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 3}))
+        return
+    rpa.load_library()
+    bound = WORKLOAD_BOUND[args.workload]
+    log(f"[bench] building {args.workload} inputs")
+    b = wl.WORKLOADS[args.workload]()
+
+    def to_dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def to_dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    q, kn, vn = to_dev_bf16(b.q), to_dev_bf16(b.k_new), to_dev_bf16(b.v_new)
+    kc, vc = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    base_tables = to_dev_i32(b.block_tables)
+    cu, kvl = to_dev_i32(b.cu_q_lens), to_dev_i32(b.kv_lens)
+    cu_h = torch.from_numpy(np.ascontiguousarray(b.cu_q_lens, np.int32))
+    kvl_h = torch.from_numpy(np.ascontiguousarray(b.kv_lens, np.int32))
+
+    sparse = args.workload == "block_union_sparse"
+    prep_steps = []
+    if sparse:
+        mask = torch.from_numpy(b.extra["mask"]).to(dev)
+        past, ctx = b.extra["past"], b.extra["context"]
+        u_tables, u_counts, u_kvl = rpa.build_union_tables(mask, base_tables[0], past, ctx,
+                                                           b.page_size)
+        torch.cuda.synchronize()
+        att_tables = u_tables[None]
+        att_kvl = u_kvl[None]
+        att_kvl_h = u_kvl[None].cpu()
+        b.extra["compacted_kv_lens"] = att_kvl_h.numpy()
+        import oracle as _o  # noqa: F401  (only for the CPU baseline below)
+        _, _, _, sel = _o.union_tables(b.extra["mask"], b.block_tables[0], past, ctx, b.page_size)
+        b.extra["allowed"] = sel[None]
+        b.extra["union_density"] = (u_counts.cpu().numpy() / (ctx // b.page_size)).round(4).tolist()
+
+        def build_tables():
+            rpa.build_union_tables(mask, base_tables[0], past, ctx, b.page_size,
+                                   out_tables=u_tables, out_counts=u_counts, out_kv_lens=u_kvl)
+        prep_steps.append(build_tables)
+    else:
+        att_tables, att_kvl, att_kvl_h = base_tables, kvl, kvl_h
+
+    write = rpa.PreparedWriteKV(kn, vn, kc, vc, base_tables, cu, kvl, cu_q_lens_host=cu_h,
+                                kv_lens_host=kvl_h)
+    attn = rpa.PreparedAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, cu_q_lens_host=cu_h,
+                                 kv_lens_host=att_kvl_h)
+    kind = rpa.select_kernel(q, kc, att_tables, cu_h, att_kvl_h)
+    flush_buf = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def flush():
+        if flush_buf is None:
+            return
+        if args.flush == "read":
+            flush_buf.sum()
+        else:
+            flush_buf.fill_(1)
+
+    def one_step(ev=None):
+        if ev:
+            ev[0].record()
+        for p in prep_steps:
+            p()
+        write()
+        if ev:
+            ev[1].record()
+        attn()
+        if ev:
+            ev[2].record()
+
+    log(f"[bench] kernel kind {kind}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        flush()
+        one_step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush()
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ms = float(step_ms.mean())
+    attn_avg_ms = float(attn_ms.mean())
+
+    if bound == "hbm":
+        work = step_bytes(b)
+        value = work / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        ach = step_bytes(b, attention_only=True) / (attn_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        work = causal_flops(b, b.extra.get("compacted_kv_lens"))
+        value = work / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        ach = work / (attn_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = {1: "decode_kernel", 2: "prefill_kernel", 3: "mixed_kernel"}[kind] + \
+        " (+ merge_kernel when split)"
+    roof["avg_launch_ms"] = round(attn_avg_ms, 5)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(b, args.workload, bound)
+
+    cfg = {"workload": args.workload, "num_seqs": b.num_seqs, "total_q": b.total_q,
+           "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+           "page_size": b.page_size, "pool_pages": b.num_pages, "layout":
+           "seq_major" if b.layout == 0 else "kv_head_major", "seed": b.seed,
+           "sum_kv_len": int(b.kv_lens.reshape(b.num_seqs, -1)[:, 0].sum()),
+           "cache_flush": args.flush, "parallelism": "none (one GPU)"}
+    if sparse:
+        cfg["union_density"] = b.extra["union_density"]
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 values, Llama-3-8B attention shapes)",
+        "config": cfg,
+        "tokens_per_s": round(b.total_q / (ms * 1e-3), 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 5) for p in (10, 50, 90)],
+        "work_per_step": work, "wall_s_timed_loop": round(wall, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

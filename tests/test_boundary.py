@@ -115,7 +115,8 @@ def test_empty_batch_is_ok_without_device(lib):
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
 def test_no_gpu_is_an_error_not_a_fallback(lib):
     s = _shape([0, 1], [4])
-    st = _attn(lib, s)
+    ws = lib.rpa_attention_workspace_size(ctypes.byref(s))
+    st = _attn(lib, s, ws=ctypes.c_void_p(16), ws_bytes=ws)
     assert st in (2, 4), st
     assert lib.rpa_last_error().decode() != ""
 
