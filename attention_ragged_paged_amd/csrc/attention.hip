@@ -204,8 +204,9 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   const int kv_len = kv_len_of(a, b, g);
   const int past = kv_len - q_len;
   const int n_rows = q_len * a.G;
-  const int k_begin = s * a.split_dec;
-  const int k_end = min(min(kv_len, k_begin + a.split_dec), dec_item_kend(kv_len, q_len, a.G, rt));
+  const int split = even_split(max_kv_len(a, b), nsplit);
+  const int k_begin = s * split;
+  const int k_end = min(min(kv_len, k_begin + split), dec_item_kend(kv_len, q_len, a.G, rt));
   const bool fused = a.k_new != nullptr;
   const bool writer = fused && rt == n_rt - 1;  // the last row tile visits every new key
 
@@ -325,7 +326,8 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
     load_chunk(base, 0, kA, vA);
     // Two chunks per trip, register double buffer.  Every load is unconditional (the last
     // one may repeat the final chunk, an L2 hit) so that the wait before each chunk's use
-    // covers exactly that chunk's loads while the other chunk's loads stay in flight.
+    // covers exactly that chunk's loads while the other chunk's loads stay in flight.  (A
+    // third buffer measured no faster: the stream is not latency-bound here.)
     for (int i = 0; i + 1 < n; i += 2) {
       load_chunk(base, i + 1, kB, vB);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this chunk's math
@@ -464,8 +466,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   const int past = kv_len - q_len;
   const int t_first = qt * a.pf_tokens;
   const int t_last = min(q_len - 1, t_first + a.pf_tokens - 1);
-  const int k_begin = s * a.split_pf;
-  const int k_end = min(min(kv_len, k_begin + a.split_pf), past + t_last + 1);
+  const int split = even_split(max_kv_len(a, b), nsplit);
+  const int k_begin = s * split;
+  const int k_end = min(min(kv_len, k_begin + split), past + t_last + 1);
   const int n_tiles = k_end > k_begin ? ceil_div(k_end - k_begin, kPrefillKeys) : 0;
   const bool fused = a.k_new != nullptr;
   const bool writer = fused && qt == n_qt - 1;  // the last query tile visits every new key
@@ -687,7 +690,10 @@ constexpr size_t kSmemBytes =
     sizeof(DecodeSmem<D>) > sizeof(PrefillSmem<D>) ? sizeof(DecodeSmem<D>) : sizeof(PrefillSmem<D>);
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnArgs a) {
+#ifndef RPA_DECODE_MIN_BLOCKS
+#define RPA_DECODE_MIN_BLOCKS 2
+#endif
+__global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   decode_item<D>(a, blockIdx.x, smem);
 }

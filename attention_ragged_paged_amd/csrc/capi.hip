@@ -65,10 +65,11 @@ int cdiv(long long x, long long y) { return (int)((x + y - 1) / y); }
 constexpr int kDecodeRowsMax = 16;
 // Largest number of KV splits of one sequence (one merge wave holds one split per lane).
 constexpr int kMaxSplits = 64;
-// Work items the split sizes aim for: several workgroups per compute unit of the
-// 256-CU chip so the tail of a ragged batch stays short.
+// Work items the split sizes aim for: a few workgroups per compute unit of the 256-CU chip.
+// Fewer, longer items amortise each item's fixed cost (work lookup, first loads, combine,
+// split merge); even splits keep the tail short.
 #ifndef RPA_TARGET_ITEMS
-#define RPA_TARGET_ITEMS 2048
+#define RPA_TARGET_ITEMS 1024
 #endif
 constexpr long long kTargetItems = RPA_TARGET_ITEMS;
 

@@ -81,6 +81,12 @@ __device__ __forceinline__ int num_splits_pf(const AttnArgs &a, int b) {
   return max(1, ceil_div(max_kv_len(a, b), a.split_pf));
 }
 
+// Keys per split of a sequence cut into nsplit splits: the range is shared out evenly (in
+// multiples of 64 keys), so no split is a short leftover that would trail the others.
+__device__ __forceinline__ int even_split(int max_kv, int nsplit) {
+  return ceil_div(ceil_div(max_kv, nsplit), 64) * 64;
+}
+
 struct ItemRef {
   int b;    // sequence, or -1 when the id is past the last item
   int rem;  // index of the item within its sequence
