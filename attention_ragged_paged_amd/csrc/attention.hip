@@ -570,14 +570,16 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
         st[mb] = mfma32x32x16(as_bf16x8(kv), qf[ks], st[mb]);
       }
     }
-    // Scale, mask (only tiles that reach past some row's limit or the range end), max.
+    // Mask (only tiles that reach past some row's limit or the range end) and row max, on
+    // the raw scores: the scale is positive, so it is applied once to the max and folded
+    // into the exponent below as one FMA per score.
     const bool need_mask = kt0 + kPrefillKeys > k_end || kt0 + kPrefillKeys - 1 > past + t_first;
     float mloc = kNegInf;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = st[mb][v] * a.scale_log2;
+        float x = st[mb][v];
         if (need_mask) {
           const int key = kt0 + 32 * mb + 8 * (v >> 2) + 4 * hf + (v & 3);
           x = (key < k_end && key < row_lim) ? x : kNegInf;
@@ -585,10 +587,20 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
         st[mb][v] = x;
         mloc = fmaxf(mloc, x);
       }
-    mloc = wave_max_xor(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    mloc = wave_max_xor(mloc, 32) * a.scale_log2;
+    // Lazy rescale: the running max only moves when a row's max grows by more than 8
+    // (log2 units), so probabilities stay below 2^8 and most tiles skip the rescale of the
+    // accumulators entirely (the final normalisation divides by l against the same max).
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) acc[md] = acc[md] * alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -598,17 +610,14 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       uint32_t w4[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = fast_exp2(st[mb][v0 + e] - m_use);
-        const float p1 = fast_exp2(st[mb][v0 + e + 1] - m_use);
+        const float p0 = fast_exp2(__builtin_fmaf(st[mb][v0 + e], a.scale_log2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(st[mb][v0 + e + 1], a.scale_log2, -m_use));
         psum += p0 + p1;
         w4[e >> 1] = pack_bf16x2(p0, p1);
       }
       pb[kb] = as_bf16x8(u32x4{w4[0], w4[1], w4[2], w4[3]});
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) acc[md] = acc[md] * alpha;
+    l_run += psum;
 
     // O^T += V^T P^T.  Lane (i = l%16, quarter q = l/16): half h = q/2 picks keys
     // 16kb + 4h + (0..3) and + 8; q%2 picks the 16-dim half of the 32-dim block.

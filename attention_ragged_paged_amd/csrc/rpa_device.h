@@ -128,13 +128,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// 16-byte chunk c of row r of an LDS tile stored row-major with D bf16 per row.  The
-// chunk index is XOR-swizzled with the row so that the same chunk of 16 consecutive rows
-// falls in different LDS banks (column reads of the MFMA operand layouts are conflict-free).
+// 16-byte chunk c of row r of an LDS tile stored row-major with D bf16 per row, XOR-swizzled
+// by a function of the row so that, for every read the kernels issue, each 256-byte LDS
+// pass touches distinct banks:
+//   - the same chunk of 16 consecutive rows (a ds_read_b128 operand column), and
+//   - 4 consecutive rows (4-aligned) x 4 consecutive chunks (4-aligned) (a transposing read),
+// while a row stays a permutation of itself (whole-row writes are conflict-free too).
+// D = 128 (16 chunks, 256-byte rows): f(r) = 4 (r mod 4) + (r / 4) mod 4.
+// D = 64 (8 chunks, two rows per bank period): the same idea on q = r / 2 within a parity.
 template <int D>
 __device__ __forceinline__ int swz_chunk(int r, int c) {
-  constexpr int kChunks = D / 8;
-  return c ^ (r & (kChunks - 1));
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    const int q = r >> 1;
+    return c ^ (((q & 1) << 2) | ((q >> 1) & 3));
+  }
 }
 
 template <int D>
