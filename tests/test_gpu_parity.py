@@ -177,12 +177,14 @@ def test_union_tables_bit_exact(seed, Hq, Hkv, nQB, nKB, S, past, kv_len, dens):
     assert np.array_equal(k.cpu().numpy(), ek)
 
 
-@pytest.mark.parametrize("column_shared", [False, True])
-def test_block_union_sparse_full_size(column_shared):
-    """Union tables built on the GPU, chunk K/V written through the base tables, then causal
-    attention over the selected KV-head-major pages; sampled rows against the oracle's
-    position-wise sparse attention."""
-    say(f"block_union_sparse full size column_shared={column_shared}")
+@pytest.mark.parametrize("column_shared,fused", [(False, False), (True, True)])
+def test_block_union_sparse_full_size(column_shared, fused):
+    """Union tables built on the GPU, then causal attention over the selected KV-head-major
+    pages; the chunk's K/V are written either by the separate scatter through the base tables
+    or inside the attention launch through the compacted tables (whose last blocks are the
+    chunk's own pages).  Caches bit-exact, sampled rows against the oracle's position-wise
+    sparse attention."""
+    say(f"block_union_sparse full size column_shared={column_shared} fused={fused}")
     b = wl.block_union_sparse(column_shared=column_shared)
     past, ctx = b.extra["past"], b.extra["context"]
     d = Dev(b)
@@ -193,14 +195,17 @@ def test_block_union_sparse_full_size(column_shared):
                                           b.page_size)
     assert np.array_equal(t.cpu().numpy(), et) and np.array_equal(kvl.cpu().numpy(), ek)
     say(f"  union density per KV head: {np.round(ec / (ctx // b.page_size), 3).tolist()}")
-    d.write()
-    out = d.attention(fused_write=False, tables=t[None].contiguous(),
+    if not fused:
+        d.write()
+    out = d.attention(fused_write=fused, tables=t[None].contiguous(),
                       kv_lens=kvl[None].contiguous(),
                       kv_lens_host=torch.from_numpy(ek[None].copy()))
     kc, vc = oracle_after_write(b)
+    assert np.array_equal(to_host_bits(d.k_cache), kc), "K cache differs"
+    assert np.array_equal(to_host_bits(d.v_cache), vc), "V cache differs"
     rows = sample_rows(b, 96)
     ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
                            b.page_size, b.num_kv_heads, layout=wl.HEAD_MAJOR,
                            block_allowed=sel[None], rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
-    compare(got, ref, f"sparse column_shared={column_shared}")
+    compare(got, ref, f"sparse column_shared={column_shared} fused={fused}")
