@@ -413,23 +413,22 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
 //
 // A prefill item is 128 query rows of one KV head: pf_tokens = 128 / G consecutive tokens of
 // each of the G query heads of the group (wave w owns rows 32w .. 32w+31), over one KV split.
-// The workgroup walks 64-key tiles up to the causal limit of its last token.  Each tile is
-// fetched into registers one tile ahead, so the global loads of tile i+1 overlap the MFMAs
-// of tile i; block-table entries sit in a register (one per lane) and never delay a tile
-// load.  Every key row is located through the block table on its own, so a 64-key tile may
-// span several pages (page size 16 or 32 included).
+// The workgroup walks 64-key tiles up to the causal limit of its last token, with two LDS
+// buffers: the K/V rows of tile i+1 are loaded straight from global memory into one buffer
+// (no register staging) while tile i is computed from the other, so one barrier per tile
+// suffices and a tile's load latency is covered by a whole tile of compute.  Tiles below
+// every row's causal limit run a body without masking.  A 64-key tile may span several
+// pages (page size 16 or 32 included): each 1 KB load instruction looks its page up.
 //   QK^T: v_mfma_f32_32x32x16_bf16, A = K tile rows from LDS (ds_read_b128), B = Q^T in
 //         registers.  Lane l gets S^T[key 32mb + 8(v/4) + 4(l/32) + v%4][row l%32].
 //   PV:   v_mfma_f32_32x32x16_bf16, A = V^T from two transposing LDS reads, B = P^T taken
 //         from the lane's own S^T registers (k-slot e of lane half h maps to key
 //         16kb + 8(e/4) + 4h + e%4, and the V^T reads use the same order).
+// The two tile buffers live in two distinct LDS arrays, so the compiler can tell that the
+// direct loads filling one buffer never alias the reads of the other and does not make
+// those reads wait for the loads.  Each array holds a 64-key K tile, then the V tile.
 template <int D>
-struct PrefillSmem {
-  uint16_t k[kPrefillKeys * D];
-  uint16_t v[kPrefillKeys * D];
-  int last;  // split merge: this workgroup arrived last
-};
-
+constexpr int kPrefillBufBytes = 2 * kPrefillKeys * D * 2;
 template <int D>
 __device__ __forceinline__ int prefill_count(const AttnArgs &a, int b) {
   const int q_len = a.cu_q_lens[b + 1] - a.cu_q_lens[b];
@@ -437,13 +436,18 @@ __device__ __forceinline__ int prefill_count(const AttnArgs &a, int b) {
   return a.Hkv * ceil_div(q_len, a.pf_tokens) * num_splits_pf(a, b);
 }
 
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
 template <int D>
-__device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
+__device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, int *last_flag) {
   constexpr int KS = D / 16;                                // QK^T MFMAs per 32-key block
   constexpr int MD = D / 32;                                // PV output blocks of 32 dims
-  constexpr int LOADS = kPrefillKeys * (D / 8) / kThreads;  // 16-byte loads per thread per tile
-  constexpr int kChunks = D / 8;
-  PrefillSmem<D> &sm = *reinterpret_cast<PrefillSmem<D> *>(smem_raw);
+  constexpr int kChunks = D / 8;                            // 16-byte chunks per row
+  constexpr int RPI = 64 / kChunks;                         // rows per 1 KB LDS load instruction
+  constexpr int LPW = kPrefillKeys / RPI / 4;               // load instructions per wave per tile
+  uint16_t *const kbuf[2] = {reinterpret_cast<uint16_t *>(lds0), reinterpret_cast<uint16_t *>(lds1)};
+  uint16_t *const vbuf[2] = {kbuf[0] + kPrefillKeys * D, kbuf[1] + kPrefillKeys * D};
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -470,6 +474,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   const int k_begin = s * split;
   const int k_end = min(min(kv_len, k_begin + split), past + t_last + 1);
   const int n_tiles = k_end > k_begin ? ceil_div(k_end - k_begin, kPrefillKeys) : 0;
+  // Tiles whose keys are all below every row's causal limit (and inside the range) need no mask.
+  const int lim_all = min(k_end, past + t_first + 1);
+  const int n_full = min(n_tiles, lim_all > k_begin ? (lim_all - k_begin) / kPrefillKeys : 0);
   const bool fused = a.k_new != nullptr;
   const bool writer = fused && qt == n_qt - 1;  // the last query tile visits every new key
 
@@ -508,57 +515,86 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
     const int blk = blk0 + lane;
     pg_lane = blk < blk_end ? table_at(a, b, g, blk) : 0;
     pg_blk0 = blk0;
+    // Wait here, once per window: otherwise every page lookup would wait for all loads in
+    // flight, the tile loads included.
+    wait_all_memory();
   };
-  // Per-thread tile rows: load u covers chunk (u*256 + tid) of the 64 x D tile.
-  u32x4 kr[LOADS], vr[LOADS];
-  int64_t roff[LOADS];  // cache offsets of the rows just fetched (for the fused write)
-  auto fetch_tile = [&](int tile) {
+  // Tile loads go straight from global memory into LDS: one instruction fills 1 KB, i.e.
+  // RPI = 64 / (D/8) consecutive rows, lane l taking 16 bytes of row l / (D/8).  Wave w issues
+  // instructions i = 4u + w.  An instruction's rows share one page (pages hold at least 16
+  // rows), so its page comes from the table window with one readlane.  The lane's LDS slot is
+  // fixed, so it loads the global chunk that the row's swizzle puts in that slot; the swizzle
+  // depends on the instruction only through i mod 4, i.e. through w, so the chunk is a
+  // per-lane constant.
+  const int ld_row = lane / kChunks;                                    // row within an instruction
+  const int ld_c8 = swz_chunk<D>(RPI * w + ld_row, lane % kChunks) * 8;  // global element offset
+  const int grp_last = (k_end - 1) & ~(RPI - 1);  // last instruction group holding a key of the range
+  auto issue_tile = [&](int tile, auto par) {  // par: the tile's buffer, tile & 1
+    constexpr int buf = decltype(par)::value;
     const int kt0 = k_begin + tile * kPrefillKeys;
     const int last_blk = (min(kt0 + kPrefillKeys, k_end) - 1) >> a.page_shift;
     if (last_blk - pg_blk0 >= 64) fetch_pages(kt0 >> a.page_shift);
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cid = u * kThreads + tid;
-      const int pos = min(kt0 + cid / kChunks, k_end - 1);
-      const int page = __shfl(pg_lane, (pos >> a.page_shift) - pg_blk0);
-      roff[u] = kv_row_offset(a, page, pos & page_mask, g) + (cid % kChunks) * 8;
-      const uint16_t *kp = a.k_cache + roff[u];
-      const uint16_t *vp = a.v_cache + roff[u];
-      if (fused && pos >= past) {
-        const int64_t noff = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + (cid % kChunks) * 8;
-        kp = a.k_new + noff;
-        vp = a.v_new + noff;
+    for (int u = 0; u < LPW; ++u) {
+      const int i = 4 * u + w;
+      const int g0 = min(kt0 + RPI * i, grp_last);  // groups past the range reload the last one
+      // rows past the range repeat its last key (their probabilities are zero; the slots past
+      // a sequence's end may hold anything, so they are never loaded)
+      const int lr = g0 + RPI > k_end ? min(ld_row, k_end - 1 - g0) : ld_row;
+      const uint16_t *ksrc, *vsrc;
+      if (fused && g0 >= past) {
+        const int64_t nb = ((int64_t)(q0 + g0 - past) * a.Hkv + g) * D;
+        const int lo = lr * a.Hkv * D + ld_c8;
+        ksrc = a.k_new + nb + lo;
+        vsrc = a.v_new + nb + lo;
+      } else {
+        const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+        const int64_t cb = kv_row_offset(a, page, g0 & page_mask, g);
+        const int lo = (int)(lr * a.slot_stride) + ld_c8;
+        ksrc = a.k_cache + cb + lo;
+        vsrc = a.v_cache + cb + lo;
+        if (fused && g0 + RPI > past) {
+          // the group straddles the first new key: its new rows come from k_new / v_new
+          const int pos = g0 + lr;
+          if (pos >= past) {
+            const int64_t no = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + ld_c8;
+            ksrc = a.k_new + no;
+            vsrc = a.v_new + no;
+          }
+        }
       }
-      kr[u] = *reinterpret_cast<const u32x4 *>(kp);
-      vr[u] = *reinterpret_cast<const u32x4 *>(vp);
+      load_lds16(ksrc, kbuf[buf] + i * RPI * D);
+      load_lds16(vsrc, vbuf[buf] + i * RPI * D);
     }
   };
-
-  if (n_tiles > 0) {
-    fetch_pages(blk_begin);
-    fetch_tile(0);
-  }
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // The item owning the sequence's last query rows stores the tile's new keys from LDS into
+  // their page slots (the page window still covers the tile).
+  auto write_new_rows = [&](int tile, auto par) {
+    constexpr int buf = decltype(par)::value;
     const int kt0 = k_begin + tile * kPrefillKeys;
-    __syncthreads();  // the previous tile's LDS reads are done
+    if (kt0 + kPrefillKeys <= past) return;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
+    for (int u = 0; u < kPrefillKeys * kChunks / kThreads; ++u) {
       const int cid = u * kThreads + tid;
       const int key = cid / kChunks;
       const int c = cid % kChunks;
       const int pos = kt0 + key;
-      *reinterpret_cast<u32x4 *>(&sm.k[lds_off<D>(key, c)]) = kr[u];
-      const bool ok = pos < k_end;
-      *reinterpret_cast<u32x4 *>(&sm.v[lds_off<D>(key, c)]) = ok ? vr[u] : u32x4{0u, 0u, 0u, 0u};
-      if (writer && ok && pos >= past) {
-        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + roff[u]) = kr[u];
-        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + roff[u]) = vr[u];
+      const int page = __shfl(pg_lane, (pos >> a.page_shift) - pg_blk0);  // every lane takes part
+      if (pos >= past && pos < k_end) {
+        const int64_t off = kv_row_offset(a, page, pos & page_mask, g) + c * 8;
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + off) =
+            *reinterpret_cast<const u32x4 *>(kbuf[buf] + lds_off<D>(key, c));
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + off) =
+            *reinterpret_cast<const u32x4 *>(vbuf[buf] + lds_off<D>(key, c));
       }
     }
-    __syncthreads();
-    if (tile + 1 < n_tiles) fetch_tile(tile + 1);
+  };
 
-    // S^T = K Q^T for the 64-key tile: two 32-key blocks.
+  // One 64-key tile from LDS buffer tile & 1: S^T, (mask), online softmax, O^T += V^T P^T.
+  auto compute_tile = [&](int tile, auto par, auto masked) {
+    const int kt0 = k_begin + tile * kPrefillKeys;
+    const uint16_t *kt = kbuf[decltype(par)::value];
+    const uint16_t *vt = vbuf[decltype(par)::value];
     f32x16 st[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -566,25 +602,23 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       for (int v = 0; v < 16; ++v) st[mb][v] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kv = *reinterpret_cast<const u32x4 *>(&sm.k[lds_off<D>(32 * mb + r32, 2 * ks + hf)]);
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(&kt[lds_off<D>(32 * mb + r32, 2 * ks + hf)]);
         st[mb] = mfma32x32x16(as_bf16x8(kv), qf[ks], st[mb]);
       }
     }
-    // Mask (only tiles that reach past some row's limit or the range end) and row max, on
-    // the raw scores: the scale is positive, so it is applied once to the max and folded
-    // into the exponent below as one FMA per score.
-    const bool need_mask = kt0 + kPrefillKeys > k_end || kt0 + kPrefillKeys - 1 > past + t_first;
+    // Row max on the raw scores: the scale is positive, so it is applied once to the max and
+    // folded into the exponent below as one FMA per score.
     float mloc = kNegInf;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = st[mb][v];
-        if (need_mask) {
+        if constexpr (decltype(masked)::value) {
           const int key = kt0 + 32 * mb + 8 * (v >> 2) + 4 * hf + (v & 3);
           x = (key < k_end && key < row_lim) ? x : kNegInf;
+          st[mb][v] = x;
         }
-        st[mb][v] = x;
         mloc = fmaxf(mloc, x);
       }
     mloc = wave_max_xor(mloc, 32) * a.scale_log2;
@@ -601,8 +635,8 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float psum = 0.f;
     bf16x8 pb[4];
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int mb = kb >> 1;
@@ -612,12 +646,13 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
       for (int e = 0; e < 8; e += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(st[mb][v0 + e], a.scale_log2, -m_use));
         const float p1 = fast_exp2(__builtin_fmaf(st[mb][v0 + e + 1], a.scale_log2, -m_use));
-        psum += p0 + p1;
         w4[e >> 1] = pack_bf16x2(p0, p1);
+        // the row sum takes the same bf16 probabilities the P V product uses
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e >> 1]), ones,
+                                                l_run, false);
       }
       pb[kb] = as_bf16x8(u32x4{w4[0], w4[1], w4[2], w4[3]});
     }
-    l_run += psum;
 
     // O^T += V^T P^T.  Lane (i = l%16, quarter q = l/16): half h = q/2 picks keys
     // 16kb + 4h + (0..3) and + 8; q%2 picks the 16-dim half of the 32-dim block.
@@ -631,15 +666,48 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int key = 16 * kb + tr_key;
-        const s16x4 lo = lds_read_tr(&sm.v[lds_off<D>(key, c) + eo]);
-        const s16x4 hi = lds_read_tr(&sm.v[lds_off<D>(key + 8, c) + eo]);
+        const s16x4 lo = lds_read_tr(&vt[lds_off<D>(key, c) + eo]);
+        const s16x4 hi = lds_read_tr(&vt[lds_off<D>(key + 8, c) + eo]);
         const bf16x8 va = __builtin_bit_cast(
             bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
         acc[md] = mfma32x32x16(va, pb[kb], acc[md]);
       }
     }
+  };
+  // Tile i: (writer: store its new keys), issue tile i+1 into the other buffer, compute
+  // tile i, wait for tile i+1 and meet at the barrier.  The buffer tile i+1 goes to was last
+  // read while computing tile i-1, which every wave finished before the previous barrier.
+  // Buffers are chosen at compile time (tiles are taken in pairs), which keeps the two
+  // buffers' accesses apart for the compiler.
+  auto step = [&](int tile, auto par, auto masked) {
+    constexpr int P = decltype(par)::value;
+    if (writer) write_new_rows(tile, par);
+    if (tile + 1 < n_tiles) issue_tile(tile + 1, std::integral_constant<int, 1 - P>{});
+    compute_tile(tile, par, masked);
+    wait_all_memory();
+    __syncthreads();
+  };
+  using even = std::integral_constant<int, 0>;
+  using odd = std::integral_constant<int, 1>;
+  if (n_tiles > 0) {
+    fetch_pages(blk_begin);
+    issue_tile(0, even{});
   }
+  // Nothing the prologue loaded (Q, tile 0) may still be in flight inside the loop: a wait
+  // there would also wait for the next tile's loads.
+  wait_all_memory();
+  __syncthreads();
+  int tile = 0;
+  for (; tile + 2 <= n_full; tile += 2) {
+    step(tile, even{}, bool_c<false>{});
+    step(tile + 1, odd{}, bool_c<false>{});
+  }
+  for (; tile + 2 <= n_tiles; tile += 2) {
+    step(tile, even{}, bool_c<true>{});
+    step(tile + 1, odd{}, bool_c<true>{});
+  }
+  if (tile < n_tiles) step(tile, even{}, bool_c<true>{});
 
   l_run += __shfl_xor(l_run, 32);
   const int token = q0 + t_row;
@@ -679,10 +747,10 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
   __syncthreads();
   if (tid == 0) {
     unsigned long long *ctr = a.counters + a.pf_counter_base + (int64_t)(q0 + t_first) * a.Hkv + g;
-    sm.last = arrive(ctr, a.call_tag) == (unsigned)nsplit;
+    *last_flag = arrive(ctr, a.call_tag) == (unsigned)nsplit;
   }
   __syncthreads();
-  if (!sm.last) return;
+  if (!*last_flag) return;
   constexpr int DH = D / 2;  // two threads per row, half of D each, 16 dims per pass
   const int mrow = tid >> 1;
   const int mhg = mrow / a.pf_tokens;
@@ -695,10 +763,6 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *smem_raw) {
 // =========================================================================== kernels ======
 
 template <int D>
-constexpr size_t kSmemBytes =
-    sizeof(DecodeSmem<D>) > sizeof(PrefillSmem<D>) ? sizeof(DecodeSmem<D>) : sizeof(PrefillSmem<D>);
-
-template <int D>
 #ifndef RPA_DECODE_MIN_BLOCKS
 #define RPA_DECODE_MIN_BLOCKS 2
 #endif
@@ -709,19 +773,27 @@ __global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(PrefillSmem<D>)];
-  prefill_item<D>(a, blockIdx.x, smem);
+  __shared__ __attribute__((aligned(16))) char lds0[kPrefillBufBytes<D>];
+  __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
+  __shared__ int last;
+  prefill_item<D>(a, blockIdx.x, lds0, lds1, &last);
 }
 
 // One launch for a batch holding both kinds: prefill items first (they are the longest),
-// then the decode items.
+// then the decode items, whose LDS overlays the first prefill buffer.
+template <int D>
+constexpr size_t kMixedLds0Bytes =
+    sizeof(DecodeSmem<D>) > (size_t)kPrefillBufBytes<D> ? sizeof(DecodeSmem<D>) : kPrefillBufBytes<D>;
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<D>];
+  __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
+  __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
+  __shared__ int last;
   if ((int)blockIdx.x < a.n_pf_items)
-    prefill_item<D>(a, blockIdx.x, smem);
+    prefill_item<D>(a, blockIdx.x, lds0, lds1, &last);
   else
-    decode_item<D>(a, blockIdx.x - a.n_pf_items, smem);
+    decode_item<D>(a, blockIdx.x - a.n_pf_items, lds0);
 }
 
 template <int D>

@@ -72,6 +72,14 @@ constexpr int kMaxSplits = 64;
 #define RPA_TARGET_ITEMS 1024
 #endif
 constexpr long long kTargetItems = RPA_TARGET_ITEMS;
+// In a mixed batch the prefill-class items run beside the decode items, which keep the
+// memory system busy; splitting them further only adds partial traffic and merges, and when
+// they outnumber a fraction of the workgroup slots they crowd the decode items out.  They
+// are cut into about this many items.
+#ifndef RPA_MIXED_PF_ITEMS
+#define RPA_MIXED_PF_ITEMS 128
+#endif
+constexpr long long kMixedPrefillItems = RPA_MIXED_PF_ITEMS;
 
 int kv_len_at(const rpa_shape *s, int b, int g) {
   return s->layout == RPA_LAYOUT_SEQ_MAJOR ? s->h_kv_lens[b]
@@ -179,9 +187,9 @@ int splits_of(const Plan &p, int q_len, int G, int maxkv) {
 }
 
 // A split size in keys (a multiple of 64) that cuts `units` 64-key units into about
-// kTargetItems items, never giving one sequence more than kMaxSplits splits.
-int choose_split(long long units, int longest_kv, int min_keys) {
-  long long per_item = std::max<long long>(1, (units + kTargetItems - 1) / kTargetItems);
+// `target` items, never giving one sequence more than kMaxSplits splits.
+int choose_split(long long units, int longest_kv, int min_keys, long long target = kTargetItems) {
+  long long per_item = std::max<long long>(1, (units + target - 1) / target);
   long long split = std::max<long long>(per_item * 64, min_keys);
   const long long floor_for_cap = (long long)cdiv(cdiv(longest_kv, 64), kMaxSplits) * 64;
   split = std::max(split, floor_for_cap);
@@ -230,7 +238,7 @@ Plan make_plan(const rpa_shape *s) {
       // the chip; prefill units are 8x the rows of decode units, so aim 8x fewer items.
       p.split_pf = choose_split(pf_units * 8, pf_longest, 1024);
     else
-      p.split_pf = choose_split(pf_units * 8, pf_longest, 512);
+      p.split_pf = choose_split(pf_units, pf_longest, 512, kMixedPrefillItems);
   }
   for (int b = 0; b < s->num_seqs; ++b) {
     const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];

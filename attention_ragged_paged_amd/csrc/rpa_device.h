@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rpa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -156,6 +158,12 @@ __device__ __forceinline__ int lds_off(int r, int c) {  // offset in bf16 elemen
 // it receives column i, i.e. the 4 elements (row 0..3, column i).
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RPA_LDS s16x4 *)(p));
+}
+
+// Direct global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes land at
+// lds_base + 16 l.  lds_base must be the same in every lane of the wave.
+__device__ __forceinline__ void load_lds16(const uint16_t *src, uint16_t *lds_base) {
+  __builtin_amdgcn_global_load_lds((const void *)src, (RPA_LDS void *)lds_base, 16, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
