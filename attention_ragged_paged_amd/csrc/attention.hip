@@ -541,30 +541,40 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       // rows past the range repeat its last key (their probabilities are zero; the slots past
       // a sequence's end may hold anything, so they are never loaded)
       const int lr = g0 + RPI > k_end ? min(ld_row, k_end - 1 - g0) : ld_row;
-      const uint16_t *ksrc, *vsrc;
+      // Address = group base (uniform) + lane byte offset (32-bit), the form the load
+      // instruction takes directly (scalar base, vector offset).
+      const uint16_t *kbase, *vbase;
+      uint32_t lo;
       if (fused && g0 >= past) {
         const int64_t nb = ((int64_t)(q0 + g0 - past) * a.Hkv + g) * D;
-        const int lo = lr * a.Hkv * D + ld_c8;
-        ksrc = a.k_new + nb + lo;
-        vsrc = a.v_new + nb + lo;
+        kbase = a.k_new + nb;
+        vbase = a.v_new + nb;
+        lo = (uint32_t)(lr * a.Hkv * D + ld_c8) * 2u;
       } else {
         const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
         const int64_t cb = kv_row_offset(a, page, g0 & page_mask, g);
-        const int lo = (int)(lr * a.slot_stride) + ld_c8;
-        ksrc = a.k_cache + cb + lo;
-        vsrc = a.v_cache + cb + lo;
-        if (fused && g0 + RPI > past) {
-          // the group straddles the first new key: its new rows come from k_new / v_new
-          const int pos = g0 + lr;
-          if (pos >= past) {
-            const int64_t no = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + ld_c8;
-            ksrc = a.k_new + no;
-            vsrc = a.v_new + no;
-          }
-        }
+        kbase = a.k_cache + cb;
+        vbase = a.v_cache + cb;
+        lo = (uint32_t)((int)(lr * a.slot_stride) + ld_c8) * 2u;
       }
-      load_lds16(ksrc, kbuf[buf] + i * RPI * D);
-      load_lds16(vsrc, vbuf[buf] + i * RPI * D);
+      if (fused && g0 < past && g0 + RPI > past) {
+        // the group straddles the first new key: its new rows come from k_new / v_new
+        const int pos = g0 + lr;
+        const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kbase) + lo);
+        const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vbase) + lo);
+        if (pos >= past) {
+          const int64_t no = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + ld_c8;
+          ksrc = a.k_new + no;
+          vsrc = a.v_new + no;
+        }
+        load_lds16(ksrc, kbuf[buf] + i * RPI * D);
+        load_lds16(vsrc, vbuf[buf] + i * RPI * D);
+      } else {
+        load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kbase) + lo),
+                   kbuf[buf] + i * RPI * D);
+        load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vbase) + lo),
+                   vbuf[buf] + i * RPI * D);
+      }
     }
   };
   // The item owning the sequence's last query rows stores the tile's new keys from LDS into
@@ -590,33 +600,56 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     }
   };
 
+  // LDS read addresses that do not change from tile to tile (bytes).
+  const int k_rd_base = lds_off<D>(r32, hf) * 2;
+  const int i16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int tr_key = 4 * (q4 >> 1) + (i16 >> 2);
+  const int tr_c0 = 2 * (q4 & 1) + ((i16 & 3) >> 1);
+  const int v_rd_lo = (lds_off<D>(tr_key, tr_c0) + 4 * (i16 & 1)) * 2;
+  const int v_rd_hi = (lds_off<D>(tr_key + 8, tr_c0) + 4 * (i16 & 1)) * 2;
+
   // One 64-key tile from LDS buffer tile & 1: S^T, (mask), online softmax, O^T += V^T P^T.
   auto compute_tile = [&](int tile, auto par, auto masked) {
     const int kt0 = k_begin + tile * kPrefillKeys;
     const uint16_t *kt = kbuf[decltype(par)::value];
     const uint16_t *vt = vbuf[decltype(par)::value];
+    // K operand reads: row 32mb + r32, logical chunk 2ks + hf.  The swizzle XORs the chunk
+    // index with a function of the row that is the same for both mb, so the byte address is
+    // (k_rd_base ^ 32 ks) + 64 D mb: one VALU op per read.
+    const char *kbytes = reinterpret_cast<const char *>(kt);
     f32x16 st[2];
+    u32x4 kf[2 * KS];
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i)
+      kf[i] = *reinterpret_cast<const u32x4 *>(kbytes + ((k_rd_base ^ (32 * (i % KS))) + 64 * D * (i / KS)));
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[mb][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kv = *reinterpret_cast<const u32x4 *>(&kt[lds_off<D>(32 * mb + r32, 2 * ks + hf)]);
-        st[mb] = mfma32x32x16(as_bf16x8(kv), qf[ks], st[mb]);
-      }
+      for (int ks = 0; ks < KS; ++ks) st[mb] = mfma32x32x16(as_bf16x8(kf[mb * KS + ks]), qf[ks], st[mb]);
     }
+    // Keep two operand reads in flight ahead of the MFMAs that consume them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     // Row max on the raw scores: the scale is positive, so it is applied once to the max and
     // folded into the exponent below as one FMA per score.
     float mloc = kNegInf;
+    const int mask_thr = min(row_lim, k_end) - kt0 - 4 * hf;  // keys kt0 + 4 hf + c, c < thr, stay
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = st[mb][v];
         if constexpr (decltype(masked)::value) {
-          const int key = kt0 + 32 * mb + 8 * (v >> 2) + 4 * hf + (v & 3);
-          x = (key < k_end && key < row_lim) ? x : kNegInf;
+          // element v of st[mb] is key kt0 + 4 hf + (32 mb + 8 (v / 4) + v % 4)
+          x = (32 * mb + 8 * (v >> 2) + (v & 3) < mask_thr) ? x : kNegInf;
           st[mb][v] = x;
         }
         mloc = fmaxf(mloc, x);
@@ -655,19 +688,24 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     }
 
     // O^T += V^T P^T.  Lane (i = l%16, quarter q = l/16): half h = q/2 picks keys
-    // 16kb + 4h + (0..3) and + 8; q%2 picks the 16-dim half of the 32-dim block.
-    const int i16 = lane & 15;
-    const int q4 = lane >> 4;
-    const int tr_key = 4 * (q4 >> 1) + (i16 >> 2);
+    // 16kb + 4h + (0..3) and + 8; q%2 picks the 16-dim half of the 32-dim block.  The read
+    // of block md, rows 16kb.. is at (v_rd ^ 64 md) + 4096 kb bytes for D = 128 (the row's
+    // swizzle is the same for every kb and XORs the chunk 4 md + c0, c0 < 4).
+    const char *vbytes = reinterpret_cast<const char *>(vt);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
-      const int c = 4 * md + 2 * (q4 & 1) + ((i16 & 3) >> 1);
-      const int eo = 4 * (i16 & 1);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int key = 16 * kb + tr_key;
-        const s16x4 lo = lds_read_tr(&vt[lds_off<D>(key, c) + eo]);
-        const s16x4 hi = lds_read_tr(&vt[lds_off<D>(key + 8, c) + eo]);
+        int alo, ahi;
+        if constexpr (D == 128) {
+          alo = (v_rd_lo ^ (64 * md)) + 32 * D * kb;
+          ahi = (v_rd_hi ^ (64 * md)) + 32 * D * kb;
+        } else {
+          alo = (lds_off<D>(16 * kb + tr_key, 4 * md + tr_c0) + 4 * (i16 & 1)) * 2;
+          ahi = (lds_off<D>(16 * kb + tr_key + 8, 4 * md + tr_c0) + 4 * (i16 & 1)) * 2;
+        }
+        const s16x4 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbytes + alo));
+        const s16x4 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbytes + ahi));
         const bf16x8 va = __builtin_bit_cast(
             bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
