@@ -529,11 +529,45 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   const int ld_row = lane / kChunks;                                    // row within an instruction
   const int ld_c8 = swz_chunk<D>(RPI * w + ld_row, lane % kChunks) * 8;  // global element offset
   const int grp_last = (k_end - 1) & ~(RPI - 1);  // last instruction group holding a key of the range
+  // Per-item constants of the tile loads.  Cache strides fit 32 bits (elements within a page
+  // and of a page); only page * page_stride needs 64.
+  const uint16_t *const kc_g = a.k_cache + (int64_t)g * a.head_stride;  // KV head g's rows
+  const uint16_t *const vc_g = a.v_cache + (int64_t)g * a.head_stride;
+  const int new_stride = a.Hkv * D;  // elements between consecutive new tokens
+  const int64_t new_row0 = ((int64_t)(q0 - past) * a.Hkv + g) * D;  // element of new key 0
+  const int pstride = (int)a.page_stride;
+  const int sstride = (int)a.slot_stride;
+  const uint32_t lo_new = (uint32_t)(ld_row * new_stride + ld_c8) * 2u;  // lane byte offsets
+  const uint32_t lo_cache = (uint32_t)(ld_row * sstride + ld_c8) * 2u;
+  auto issue_group = [&](int i, int g0, bool is_new, uint32_t lo, uint16_t *kdst, uint16_t *vdst) {
+    if (is_new) {
+      const int64_t nb = new_row0 + (int64_t)g0 * new_stride;
+      load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(a.k_new + nb) + lo), kdst);
+      load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(a.v_new + nb) + lo), vdst);
+    } else {
+      const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+      const int64_t cb = (int64_t)page * pstride + (g0 & page_mask) * sstride;
+      load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kc_g + cb) + lo), kdst);
+      load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vc_g + cb) + lo), vdst);
+    }
+  };
   auto issue_tile = [&](int tile, auto par) {  // par: the tile's buffer, tile & 1
     constexpr int buf = decltype(par)::value;
     const int kt0 = k_begin + tile * kPrefillKeys;
     const int last_blk = (min(kt0 + kPrefillKeys, k_end) - 1) >> a.page_shift;
     if (last_blk - pg_blk0 >= 64) fetch_pages(kt0 >> a.page_shift);
+    const bool all_new = fused && kt0 >= past;
+    const bool all_cached = !fused || kt0 + kPrefillKeys <= past;
+    if (kt0 + kPrefillKeys <= k_end && (all_new || all_cached)) {
+      // Common case: every group of the tile is in range and of one kind.
+#pragma unroll
+      for (int u = 0; u < LPW; ++u) {
+        const int i = 4 * u + w;
+        issue_group(i, kt0 + RPI * i, all_new, all_new ? lo_new : lo_cache,
+                    kbuf[buf] + i * RPI * D, vbuf[buf] + i * RPI * D);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int i = 4 * u + w;
@@ -541,39 +575,21 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       // rows past the range repeat its last key (their probabilities are zero; the slots past
       // a sequence's end may hold anything, so they are never loaded)
       const int lr = g0 + RPI > k_end ? min(ld_row, k_end - 1 - g0) : ld_row;
-      // Address = group base (uniform) + lane byte offset (32-bit), the form the load
-      // instruction takes directly (scalar base, vector offset).
-      const uint16_t *kbase, *vbase;
-      uint32_t lo;
-      if (fused && g0 >= past) {
-        const int64_t nb = ((int64_t)(q0 + g0 - past) * a.Hkv + g) * D;
-        kbase = a.k_new + nb;
-        vbase = a.v_new + nb;
-        lo = (uint32_t)(lr * a.Hkv * D + ld_c8) * 2u;
-      } else {
-        const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
-        const int64_t cb = kv_row_offset(a, page, g0 & page_mask, g);
-        kbase = a.k_cache + cb;
-        vbase = a.v_cache + cb;
-        lo = (uint32_t)((int)(lr * a.slot_stride) + ld_c8) * 2u;
-      }
+      uint16_t *const kdst = kbuf[buf] + i * RPI * D;
+      uint16_t *const vdst = vbuf[buf] + i * RPI * D;
       if (fused && g0 < past && g0 + RPI > past) {
-        // the group straddles the first new key: its new rows come from k_new / v_new
+        // the group straddles the first new key: every row is located on its own
         const int pos = g0 + lr;
-        const uint16_t *ksrc = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kbase) + lo);
-        const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vbase) + lo);
-        if (pos >= past) {
-          const int64_t no = ((int64_t)(q0 + pos - past) * a.Hkv + g) * D + ld_c8;
-          ksrc = a.k_new + no;
-          vsrc = a.v_new + no;
-        }
-        load_lds16(ksrc, kbuf[buf] + i * RPI * D);
-        load_lds16(vsrc, vbuf[buf] + i * RPI * D);
+        const int64_t off = pos >= past
+                                ? new_row0 + (int64_t)pos * new_stride + ld_c8
+                                : (int64_t)__builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0) *
+                                          pstride + (pos & page_mask) * sstride + ld_c8;
+        load_lds16((pos >= past ? a.k_new : kc_g) + off, kdst);
+        load_lds16((pos >= past ? a.v_new : vc_g) + off, vdst);
       } else {
-        load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kbase) + lo),
-                   kbuf[buf] + i * RPI * D);
-        load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vbase) + lo),
-                   vbuf[buf] + i * RPI * D);
+        const bool is_new = fused && g0 >= past;
+        const uint32_t lo = (uint32_t)(lr * (is_new ? new_stride : sstride) + ld_c8) * 2u;
+        issue_group(i, g0, is_new, lo, kdst, vdst);
       }
     }
   };
