@@ -230,7 +230,7 @@ def main():
     attn = rpa.PreparedAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, k_new=kn, v_new=vn,
                                  cu_q_lens_host=cu_h, kv_lens_host=att_kvl_h)
     kind = rpa.select_kernel(q, kc, att_tables, cu_h, att_kvl_h)
-    flush_buf = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush_buf = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def flush():
         if flush_buf is None:
