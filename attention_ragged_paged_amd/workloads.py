@@ -99,19 +99,27 @@ def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, pag
 
     Pages come from one permutation of ``pool_pages`` physical pages.  With
     ``poison_unused`` every cache slot that no sequence owns (unused pages and
-    the tail slots of each sequence's last page) holds bf16 NaN.
+    the tail slots of each sequence's last page) holds bf16 NaN.  In the
+    KV-head-major layout ``kv_lens`` may also be given per (sequence, KV head),
+    shape [B, Hkv] (each head with its own past, as over compacted tables).
     """
     rng = np.random.default_rng(seed) if rng is None else rng
     q_lens = np.asarray(q_lens, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     B = q_lens.shape[0]
     Hq, Hkv, D, S = num_q_heads, num_kv_heads, head_dim, page_size
-    assert kv_lens.shape == (B,) and np.all(kv_lens >= q_lens)
-    n_blocks = (kv_lens + S - 1) // S
+    if kv_lens.ndim == 1:
+        assert kv_lens.shape == (B,)
+        kv_head = np.repeat(kv_lens[:, None], Hkv, axis=1)
+    else:
+        assert layout == HEAD_MAJOR and kv_lens.shape == (B, Hkv)
+        kv_head = kv_lens
+    assert np.all(kv_head >= q_lens[:, None])
+    n_blocks_h = (kv_head + S - 1) // S            # [B, Hkv]
+    n_blocks = n_blocks_h.max(axis=1)             # per sequence (its longest head)
     if max_pages is None:
         max_pages = int(max(1, n_blocks.max(initial=1)))
-    owners = B if layout == SEQ_MAJOR else B * Hkv
-    need = int(n_blocks.sum()) * (1 if layout == SEQ_MAJOR else Hkv)
+    need = int(n_blocks.sum()) if layout == SEQ_MAJOR else int(n_blocks_h.sum())
     assert need <= pool_pages, f"pool of {pool_pages} pages < {need} needed"
     perm = rng.permutation(pool_pages).astype(np.int32)
     if layout == SEQ_MAJOR:
@@ -126,9 +134,9 @@ def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, pag
             cur += nb
         else:
             for g in range(Hkv):
-                tables[b, g, :nb] = perm[cur:cur + nb]
-                cur += nb
-    del owners
+                nbg = int(n_blocks_h[b, g])
+                tables[b, g, :nbg] = perm[cur:cur + nbg]
+                cur += nbg
     cache_shape = (pool_pages, S, Hkv, D) if layout == SEQ_MAJOR else (pool_pages, S, D)
     k_cache = _normal_bf16(rng, cache_shape)
     v_cache = _normal_bf16(rng, cache_shape)
@@ -141,14 +149,14 @@ def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, pag
     if layout == SEQ_MAJOR:
         kvl = kv_lens.astype(np.int32)
     else:
-        kvl = np.repeat(kv_lens.astype(np.int32)[:, None], Hkv, axis=1)
+        kvl = np.ascontiguousarray(kv_head.astype(np.int32))
     if poison_unused:
         owned = np.zeros((pool_pages, S), dtype=bool)
         for b in range(B):
-            L = int(kv_lens[b])
             rows = tables[b][None] if layout == SEQ_MAJOR else tables[b]
-            for row in rows:
-                for i in range(int(n_blocks[b])):
+            for gi, row in enumerate(rows):
+                L = int(kv_head[b, gi])
+                for i in range((L + S - 1) // S):
                     n = min(S, L - i * S)
                     owned[row[i], :n] = True
         k_cache[~owned] = BF16_NAN

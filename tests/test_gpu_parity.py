@@ -209,3 +209,50 @@ def test_block_union_sparse_full_size(column_shared, fused):
                            block_allowed=sel[None], rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
     compare(got, ref, f"sparse column_shared={column_shared} fused={fused}")
+
+
+# --------------------------------------------------------------- layouts and extremes ----
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_head_major_per_head_lengths(kernel):
+    """KV-head-major pages with a different kv_len (and so a different past) per KV head,
+    as over compacted tables: decode-class and prefill-class sequences, fused write."""
+    say(f"head-major per-head lengths kernel={kernel}")
+    qs = [1, 40, 3]
+    kv = np.array([[70, 33], [40, 95], [3, 130]])
+    pool = int(((kv + 15) // 16).sum()) + 4
+    b = wl.ragged_batch("hm", qs, kv, 8, 2, 128, 16, pool, 77, layout=wl.HEAD_MAJOR)
+    _full_check(b, kernel=kernel, label=f"head-major kernel={kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_group_of_64_heads(kernel):
+    """G = 64 query heads per KV head: every sequence is prefill-class (2 tokens per 128-row
+    tile); forcing the decode kernel still gives the same result."""
+    say(f"G=64 kernel={kernel}")
+    b = wl.ragged_batch("g64", [1, 3, 20], [101, 503, 57], 64, 1, 64, 32, 30, 78)
+    _full_check(b, kernel=kernel, label=f"G=64 kernel={kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_page_size_1024(kernel):
+    say(f"page 1024 kernel={kernel}")
+    b = wl.ragged_batch("p1024", [1, 30], [3001, 2030], 8, 2, 128, 1024, 8, 79)
+    _full_check(b, kernel=kernel, label=f"page 1024 kernel={kernel}")
+
+
+def test_long_context_prefill_splits():
+    """Prefill-only batch whose long contexts are cut into many KV splits (merged in-kernel)."""
+    say("long-context prefill splits")
+    b = wl.ragged_batch("lcp", [200, 64], [30200, 5064], 32, 8, 128, 16, 2300, 80)
+    d = Dev(b)
+    assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_PREFILL
+    del d
+    _sampled(b, 160, "long-context prefill")
+
+
+def test_long_context_mixed_splits():
+    """Mixed batch with a chunk at a 40k context and decodes up to 70k keys."""
+    say("long-context mixed splits")
+    b = wl.ragged_batch("lcm", [300, 1, 1, 1], [40300, 9001, 101, 70001], 32, 8, 128, 16, 7500, 81)
+    _sampled(b, 160, "long-context mixed")
