@@ -670,7 +670,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
         }
         mloc = fmaxf(mloc, x);
       }
-    mloc = wave_max_xor(mloc, 32) * a.scale_log2;
+    mloc = pair_max32(mloc) * a.scale_log2;
     // Lazy rescale: the running max only moves when a row's max grows by more than 8
     // (log2 units), so probabilities stay below 2^8 and most tiles skip the rescale of the
     // accumulators entirely (the final normalisation divides by l against the same max).
@@ -763,7 +763,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   }
   if (tile < n_tiles) step(tile, even{}, bool_c<true>{});
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = pair_sum32(l_run);  // the row sum over both lane halves
   const int token = q0 + t_row;
   if (nsplit == 1) {
     if (!row_ok) return;

@@ -184,4 +184,16 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// Max / sum over the lane pair (l, l ^ 32) with the gfx950 half swap (one VALU op, no LDS
+// round trip): the swap of (v, v) returns v's low half in both halves of its first result
+// and v's high half in both halves of its second.
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace rpa
