@@ -634,6 +634,10 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     // index with a function of the row that is the same for both mb, so the byte address is
     // (k_rd_base ^ 32 ks) + 64 D mb: one VALU op per read.
     const char *kbytes = reinterpret_cast<const char *>(kt);
+    // The score MFMAs issue at raised wave priority, so that on a SIMD shared by two waves
+    // the one entering its MFMA phase goes first and the other's softmax VALU work runs
+    // beside the MFMAs (measured: block-union sparse 6% faster, prefill 2%).
+    __builtin_amdgcn_s_setprio(1);
     f32x16 st[2];
     u32x4 kf[2 * KS];
 #pragma unroll
@@ -654,6 +658,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_s_setprio(0);
     // Row max on the raw scores: the scale is positive, so it is applied once to the max and
     // folded into the exponent below as one FMA per score.
     float mloc = kNegInf;
