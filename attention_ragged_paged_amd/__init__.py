@@ -7,8 +7,10 @@ CPU fallback: every call fails loudly if the library or a gfx950 device is missi
     write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, ...)
     attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, ...)
     build_union_tables(mask, base_tables, past, kv_len, page_size)
+    GraphAttention(...)   # device-planned call that a HIP graph can capture
 """
 from ._rpa import (  # noqa: F401
+    GraphAttention,
     KERNEL_AUTO,
     KERNEL_DECODE,
     KERNEL_MIXED,

@@ -25,7 +25,8 @@ _STATUS = {0: "RPA_OK", 1: "RPA_ERR_INVALID_ARGUMENT", 2: "RPA_ERR_UNSUPPORTED",
            3: "RPA_ERR_WORKSPACE_TOO_SMALL", 4: "RPA_ERR_HIP"}
 
 EXPORTED = ("rpa_write_kv", "rpa_attention_workspace_size", "rpa_select_kernel", "rpa_attention",
-            "rpa_build_union_tables", "rpa_last_error")
+            "rpa_graph_workspace_size", "rpa_graph_attention", "rpa_build_union_tables",
+            "rpa_last_error")
 
 
 class RpaError(RuntimeError):
@@ -49,6 +50,12 @@ class RpaShape(ctypes.Structure):
         ("h_cu_q_lens", ctypes.POINTER(ctypes.c_int32)),
         ("h_kv_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
+
+
+class RpaGraphShape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "max_seqs", "max_tokens", "max_splits", "num_q_heads", "num_kv_heads", "head_dim",
+        "page_size", "num_pages", "max_pages_per_seq", "layout")]
 
 
 _lib = None
@@ -76,6 +83,12 @@ def load_library():
     lib.rpa_select_kernel.restype = i32
     lib.rpa_attention.argtypes = [shp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.rpa_attention.restype = ctypes.c_int
+    gshp = ctypes.POINTER(RpaGraphShape)
+    lib.rpa_graph_workspace_size.argtypes = [gshp]
+    lib.rpa_graph_workspace_size.restype = sz
+    lib.rpa_graph_attention.argtypes = [gshp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                        vp, sz, vp]
+    lib.rpa_graph_attention.restype = ctypes.c_int
     lib.rpa_build_union_tables.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.rpa_build_union_tables.restype = ctypes.c_int
     lib.rpa_last_error.argtypes = []
@@ -276,3 +289,42 @@ class PreparedWriteKV:
 
     def __call__(self):
         _check(self.lib.rpa_write_kv(*self.args))
+
+
+class GraphAttention:
+    """rpa_graph_attention over fixed buffers: a call reads no host data, so it can be captured
+    in a HIP graph (torch.cuda.graph) and replayed after the buffers' device contents change.
+
+    The buffers fix the bounds: q and out have max_tokens rows, cu_q_lens has max_seqs + 1
+    entries (sequences past the live batch repeat the last offset and have kv_len 0), kv_lens
+    and block_tables max_seqs rows.  The workspace (state that persists from call to call) is
+    allocated zeroed here.  Every call enqueues on the current stream at call time.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *,
+                 k_new=None, v_new=None, out=None, max_splits=16):
+        self.lib = load_library()
+        _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                     cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
+        layout, Hkv, S, D = _cache_geometry(k_cache, block_tables)
+        self.shape = RpaGraphShape(cu_q_lens.numel() - 1, q.shape[0], max_splits, q.shape[1], Hkv,
+                                   D, S, k_cache.shape[0], block_tables.shape[-1], layout)
+        need = self.lib.rpa_graph_workspace_size(ctypes.byref(self.shape))
+        if need == ctypes.c_size_t(-1).value:
+            _check(1)
+        self.workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        self.out = torch.empty_like(q) if out is None else out
+        self.device = q.device
+        self.keep = (q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, k_new, v_new)
+        self.args = (ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                     _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens), ctypes.c_float(scale),
+                     _ptr(k_new), _ptr(v_new), _ptr(self.out), _ptr(self.workspace),
+                     ctypes.c_size_t(need))
+
+    def __call__(self):
+        _check(self.lib.rpa_graph_attention(*self.args, _stream(self.device)))
+        return self.out
+
+    def status(self) -> int:
+        """The planning kernel's status word of the last call (0: the batch was valid)."""
+        return int(self.workspace[:4].view(torch.int32).item())

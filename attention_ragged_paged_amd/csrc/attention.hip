@@ -881,3 +881,165 @@ hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blo
 }
 
 }  // namespace rpa
+
+// ===================================================================== graph-capturable ======
+//
+// One persistent launch that plans on the device.  Every workgroup reads the batch lengths
+// and derives, redundantly, the same plan the host planner derives from its mirrors
+// (decode-class sequences: q_len * G <= 16; KV split sizes cutting the work into about
+// target_items decode items and, for prefill-class work, about mixed_pf_items items beside
+// decode work or 8x fewer, 1024-key minimum, alone), with at most max_splits splits per
+// sequence.  Workgroup w runs item w first and then takes items from a queue; the last
+// workgroup to leave resets the queue and advances the call tag for the next call.
+namespace rpa {
+
+__device__ __forceinline__ int g_choose_split(long long units, int longest_kv, int min_keys,
+                                              long long target, int max_splits) {
+  const long long per_item = max(1ll, (units + target - 1) / target);
+  long long split = max(per_item * 64, (long long)min_keys);
+  const long long floor_for_cap = (long long)ceil_div(ceil_div(longest_kv, 64), max_splits) * 64;
+  split = max(split, floor_for_cap);
+  return (int)min(split, (long long)(1 << 30));
+}
+
+// Sum / max over the workgroup (kThreads threads); red holds kThreads / 64 slots.
+template <class T, class Op>
+__device__ __forceinline__ T block_reduce(T v, Op op, T *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off));
+  __syncthreads();  // red is free (an earlier reduction's readers are done)
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = op(r, red[w]);
+  return r;
+}
+
+struct GraphCall {
+  uint32_t status;
+  int split_dec, split_pf, n_pf_items, n_items;
+};
+
+__device__ GraphCall plan_graph_call(const GraphPlanArgs &p, long long *red) {
+  const int tid = threadIdx.x;
+  // q_len and the longest kv_len of sequence b; bad when a length breaks a precondition.
+  auto seq = [&](int b, int &q_len, int &kv_max) {
+    q_len = p.cu_q_lens[b + 1] - p.cu_q_lens[b];
+    kv_max = 0;
+    bool bad = q_len < 0;
+    const int heads = p.kvl_head_stride ? p.Hkv : 1;
+    for (int g = 0; g < heads; ++g) {
+      const int kv = p.kv_lens[b * p.kvl_seq_stride + g * p.kvl_head_stride];
+      bad |= kv < q_len || ceil_div(kv, p.page_size) > p.max_pages;
+      kv_max = max(kv_max, kv);
+    }
+    return bad;
+  };
+  auto add = [](long long x, long long y) { return x + y; };
+  auto mx = [](long long x, long long y) { return max(x, y); };
+  long long bad = 0, dec_units = 0, pf_units = 0, dec_long = 0, pf_long = 0;
+  for (int b = tid; b < p.B; b += kThreads) {
+    int q_len, kv;
+    if (seq(b, q_len, kv)) bad |= 4;
+    if (q_len <= 0) continue;
+    if ((long long)q_len * p.G <= kDecodeRows) {
+      dec_units += (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * ceil_div(kv, 64);
+      dec_long = max(dec_long, (long long)kv);
+    } else {
+      pf_units += (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * ceil_div(kv, 64);
+      pf_long = max(pf_long, (long long)kv);
+    }
+  }
+  if (tid == 0) {
+    if (p.cu_q_lens[0] != 0) bad |= 1;
+    if (p.cu_q_lens[p.B] > p.T_max) bad |= 2;
+  }
+  bad = block_reduce(bad, [](long long x, long long y) { return x | y; }, red);
+  dec_units = block_reduce(dec_units, add, red);
+  pf_units = block_reduce(pf_units, add, red);
+  dec_long = block_reduce(dec_long, mx, red);
+  pf_long = block_reduce(pf_long, mx, red);
+  GraphCall c;
+  c.status = (uint32_t)bad;
+  c.split_dec = dec_units > 0 ? g_choose_split(dec_units, (int)dec_long, 256, p.target_items, p.max_splits)
+                              : (1 << 30);
+  c.split_pf = pf_units == 0 ? (1 << 30)
+               : dec_units > 0 ? g_choose_split(pf_units, (int)pf_long, 512, p.mixed_pf_items, p.max_splits)
+                               : g_choose_split(pf_units * 8, (int)pf_long, 1024, p.target_items, p.max_splits);
+  long long n_dec = 0, n_pf = 0;
+  for (int b = tid; b < p.B; b += kThreads) {
+    int q_len, kv;
+    seq(b, q_len, kv);
+    if (q_len <= 0) continue;
+    if ((long long)q_len * p.G <= kDecodeRows)
+      n_dec += (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
+    else
+      n_pf += (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * max(1, ceil_div(kv, c.split_pf));
+  }
+  n_dec = block_reduce(n_dec, add, red);
+  n_pf = block_reduce(n_pf, add, red);
+  c.n_pf_items = bad ? 0 : (int)n_pf;
+  c.n_items = bad ? 0 : (int)(n_pf + n_dec);
+  return c;
+}
+
+// Persistent attention: items run exactly as in the mixed kernel (prefill items first).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, GraphPlanArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
+  __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
+  __shared__ int last;
+  __shared__ int s_item;
+  GraphPlan *plan = p.plan;
+  // The tag of this call: the plan's tag is advanced only after every workgroup has left.
+  const unsigned long long tag = __hip_atomic_load(&plan->tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  const GraphCall c = plan_graph_call(p, reinterpret_cast<long long *>(lds0));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    plan->status = c.status;
+    plan->split_dec = c.split_dec;
+    plan->split_pf = c.split_pf;
+    plan->n_pf_items = c.n_pf_items;
+    plan->n_items = c.n_items;
+  }
+  AttnArgs a = args;
+  a.split_dec = c.split_dec;
+  a.split_pf = c.split_pf;
+  a.n_pf_items = c.n_pf_items;
+  a.call_tag = (tag & ((1ull << 40) - 1)) << 24;
+  int item = blockIdx.x;
+  while (item < c.n_items) {
+    if (item < c.n_pf_items)
+      prefill_item<D>(a, item, lds0, lds1, &last);
+    else
+      decode_item<D>(a, item - c.n_pf_items, lds0);
+    __syncthreads();  // the item is done with the LDS and with s_item
+    if (threadIdx.x == 0) s_item = (int)(gridDim.x + atomicAdd(&plan->queue, 1u));
+    __syncthreads();
+    item = s_item;
+  }
+  // Leaving: the queue and tag accesses of this workgroup are complete (their values were
+  // used), so the last one to arrive can reset them; the next call sees the reset after the
+  // kernel boundary.  Relaxed on purpose: an acquire/release here would write back and
+  // invalidate the L2 of the workgroup's XCD under the workgroups still running there.
+  if (threadIdx.x == 0) {
+    const uint32_t left = __hip_atomic_fetch_add(&plan->exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == gridDim.x - 1) {
+      __hip_atomic_store(&plan->queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&plan->exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&plan->tag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+hipError_t launch_graph_attention(const AttnArgs &a, const GraphPlanArgs &p, int D,
+                                  int n_workgroups, hipStream_t stream) {
+  const dim3 grid((unsigned)n_workgroups), block(kThreads);
+  if (D == 128)
+    hipLaunchKernelGGL(graph_kernel<128>, grid, block, 0, stream, a, p);
+  else
+    hipLaunchKernelGGL(graph_kernel<64>, grid, block, 0, stream, a, p);
+  return hipGetLastError();
+}
+
+}  // namespace rpa

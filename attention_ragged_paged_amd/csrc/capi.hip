@@ -417,6 +417,167 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   return ok();
 }
 
+// ----------------------------------------------------------------- graph-capturable ----
+
+}  // extern "C"
+
+namespace {
+
+rpa_status validate_graph(const rpa_graph_shape *s) {
+  if (!s) return fail(RPA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->max_seqs < 1 || s->max_tokens < 1)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "max_seqs %d and max_tokens %d must be >= 1",
+                s->max_seqs, s->max_tokens);
+  if (s->max_splits < 1 || s->max_splits > kMaxSplits)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "max_splits %d must be in [1, %d]", s->max_splits,
+                kMaxSplits);
+  if (s->num_kv_heads < 1 || s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT,
+                "num_q_heads %d must be a positive multiple of num_kv_heads %d", s->num_q_heads,
+                s->num_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RPA_ERR_UNSUPPORTED, "head_dim %d is not built (64 and 128 are)", s->head_dim);
+  if (s->num_q_heads / s->num_kv_heads > rpa::kPrefillRows)
+    return fail(RPA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per KV head",
+                s->num_q_heads / s->num_kv_heads, rpa::kPrefillRows);
+  if (!is_pow2(s->page_size) || s->page_size < 16 || s->page_size > 1024)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two in [16, 1024]",
+                s->page_size);
+  if (s->num_pages < 1 || s->max_pages_per_seq < 1)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "num_pages %d and max_pages_per_seq %d must be >= 1",
+                s->num_pages, s->max_pages_per_seq);
+  if (s->layout != RPA_LAYOUT_SEQ_MAJOR && s->layout != RPA_LAYOUT_HEAD_MAJOR)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "layout %d is not a RPA_LAYOUT_* value", s->layout);
+  return RPA_OK;
+}
+
+// Graph workspace: [plan][split partials, (m, l) pairs, counters].
+struct GraphLayout {
+  size_t plan = 0, part_o = 0, part_ml = 0, counters = 0, pf_counter_base = 0, total = 0;
+};
+
+GraphLayout graph_layout(const rpa_graph_shape *s) {
+  GraphLayout g;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  g.plan = take(sizeof(rpa::GraphPlan));
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const size_t rows = s->max_splits > 1 ? (size_t)s->max_splits * s->max_tokens * s->num_q_heads : 0;
+  g.part_o = take(rows * s->head_dim * sizeof(float));
+  g.part_ml = take(rows * 2 * sizeof(float));
+  const size_t dec_ctr = s->max_splits > 1 ? ((size_t)s->max_tokens * G + rpa::kDecodeRows) * s->num_kv_heads : 0;
+  const size_t pf_ctr = s->max_splits > 1 ? (size_t)s->max_tokens * s->num_kv_heads : 0;
+  g.pf_counter_base = dec_ctr;
+  g.counters = take((dec_ctr + pf_ctr) * sizeof(unsigned long long));
+  g.total = off;
+  return g;
+}
+
+int workgroup_slots() {  // two attention workgroups per compute unit
+  static int slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (slots[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    slots[dev] = 2 * cus;
+  }
+  return slots[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rpa_graph_workspace_size(const rpa_graph_shape *shape) {
+  if (validate_graph(shape) != RPA_OK) return (size_t)-1;
+  return graph_layout(shape).total;
+}
+
+rpa_status rpa_graph_attention(const rpa_graph_shape *shape, const void *q, void *k_cache,
+                               void *v_cache, const int32_t *block_tables,
+                               const int32_t *cu_q_lens, const int32_t *kv_lens, float scale,
+                               const void *k_new, const void *v_new, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  rpa_status st = validate_graph(shape);
+  if (st != RPA_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "scale %g must be finite and > 0", (double)scale);
+  if (!q || !k_cache || !v_cache || !block_tables || !cu_q_lens || !kv_lens || !out || !workspace)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_graph_attention: a device pointer is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "k_new and v_new must both be given or both be NULL");
+  const GraphLayout gl = graph_layout(shape);
+  if (workspace_bytes < gl.total)
+    return fail(RPA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
+                workspace_bytes, gl.total);
+  st = check_device();
+  if (st != RPA_OK) return st;
+  // The per-call values (split sizes, item counts, tag) come from the device plan.
+  rpa_shape s{};
+  s.num_seqs = shape->max_seqs;
+  s.total_q = shape->max_tokens;
+  s.num_q_heads = shape->num_q_heads;
+  s.num_kv_heads = shape->num_kv_heads;
+  s.head_dim = shape->head_dim;
+  s.page_size = shape->page_size;
+  s.num_pages = shape->num_pages;
+  s.max_pages_per_seq = shape->max_pages_per_seq;
+  s.layout = shape->layout;
+  char *ws = static_cast<char *>(workspace);
+  const bool split = shape->max_splits > 1;
+  rpa::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(k_cache);
+  a.v_cache = static_cast<const uint16_t *>(v_cache);
+  a.out = static_cast<uint16_t *>(out);
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
+  a.tables = block_tables;
+  a.cu_q_lens = cu_q_lens;
+  a.kv_lens = kv_lens;
+  a.part_o = split ? reinterpret_cast<float *>(ws + gl.part_o) : nullptr;
+  a.part_ml = split ? reinterpret_cast<float *>(ws + gl.part_ml) : nullptr;
+  a.counters = split ? reinterpret_cast<unsigned long long *>(ws + gl.counters) : nullptr;
+  a.B = shape->max_seqs;
+  a.T = shape->max_tokens;  // the partials' row layout
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.G = shape->num_q_heads / shape->num_kv_heads;
+  a.page_shift = ilog2(shape->page_size);
+  fill_layout(&s, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride, a.bt_head_stride,
+              a.kvl_seq_stride, a.kvl_head_stride);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dec_rows_max = kDecodeRowsMax;
+  a.pf_tokens = std::max(1, rpa::kPrefillRows / a.G);
+  a.pf_counter_base = (int32_t)gl.pf_counter_base;
+  rpa::GraphPlanArgs pa{};
+  pa.cu_q_lens = cu_q_lens;
+  pa.kv_lens = kv_lens;
+  pa.plan = reinterpret_cast<rpa::GraphPlan *>(ws + gl.plan);
+  pa.B = shape->max_seqs;
+  pa.T_max = shape->max_tokens;
+  pa.Hkv = a.Hkv;
+  pa.G = a.G;
+  pa.page_size = shape->page_size;
+  pa.max_pages = shape->max_pages_per_seq;
+  pa.kvl_seq_stride = a.kvl_seq_stride;
+  pa.kvl_head_stride = a.kvl_head_stride;
+  pa.pf_tokens = a.pf_tokens;
+  pa.max_splits = shape->max_splits;
+  pa.target_items = (int32_t)kTargetItems;
+  pa.mixed_pf_items = (int32_t)kMixedPrefillItems;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = rpa::launch_graph_attention(a, pa, shape->head_dim, workgroup_slots(), hs);
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "graph attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 rpa_status rpa_build_union_tables(const uint8_t *mask, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t num_q_blocks, int32_t num_kv_blocks,
                                   const int32_t *base_tables, int32_t past, int32_t kv_len,

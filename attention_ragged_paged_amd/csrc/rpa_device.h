@@ -25,6 +25,19 @@ constexpr int kDecodeRows = 16;      // query rows per decode work item (one 16x
 constexpr int kPrefillRows = 128;    // query rows per prefill work item (4 waves x 32)
 constexpr int kPrefillKeys = 64;     // keys per prefill KV tile
 
+// State of a graph-capturable call at the start of its workspace.  The queue, the exit count
+// and the tag persist from call to call (zero in a fresh workspace); the other fields report
+// the last call's plan.
+struct GraphPlan {
+  uint32_t status;                 // 0: valid batch; else bit flags of broken preconditions
+  int32_t split_dec, split_pf;     // keys per KV split (multiples of 64)
+  int32_t n_pf_items, n_items;     // prefill items come first in the item numbering
+  uint32_t queue;                  // items handed out past the first one of each workgroup
+  uint32_t exits;                  // workgroups of the running call that have left
+  uint32_t pad;
+  unsigned long long tag;          // number of calls made so far
+};
+
 // Everything the attention kernels need, passed by value as the kernel argument.
 struct AttnArgs {
   const uint16_t *q;        // [T][Hq][D] bf16

@@ -32,6 +32,24 @@ hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
                             hipStream_t stream);
 
+struct GraphPlan;
+
+struct GraphPlanArgs {
+  const int32_t *cu_q_lens;  // [B + 1]
+  const int32_t *kv_lens;
+  GraphPlan *plan;
+  int32_t B, T_max, Hkv, G;
+  int32_t page_size, max_pages;
+  int32_t kvl_seq_stride, kvl_head_stride;
+  int32_t pf_tokens, max_splits;
+  int32_t target_items, mixed_pf_items;  // the host planner's item targets
+};
+
+// Persistent attention of a graph-capturable call on n_workgroups workgroups: each derives
+// the call's plan from the lengths on the device, then the workgroups share out the items.
+hipError_t launch_graph_attention(const AttnArgs &a, const GraphPlanArgs &p, int D,
+                                  int n_workgroups, hipStream_t stream);
+
 struct UnionArgs {
   const uint8_t *mask;       // [Hq][nQB][nKB]
   const int32_t *base;       // [Hkv][nKB]

@@ -162,6 +162,10 @@ def main():
                     help="only run a plain 512 MiB device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("host", "graph"), default="host",
+                    help="host: rpa_attention planned from host mirrors (the default); graph: "
+                         "rpa_graph_attention (device-side plan + persistent kernel) captured "
+                         "once in a HIP graph and replayed every step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -229,6 +233,16 @@ def main():
     # slot for every new key as the base tables give).
     attn = rpa.PreparedAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, k_new=kn, v_new=vn,
                                  cu_q_lens_host=cu_h, kv_lens_host=att_kvl_h)
+    if args.path == "graph":
+        ga = rpa.GraphAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, k_new=kn, v_new=vn,
+                                max_splits=16)
+        ga()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ga()
+        torch.cuda.synchronize()
+        attn = graph.replay
     kind = rpa.select_kernel(q, kc, att_tables, cu_h, att_kvl_h)
     flush_buf = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
@@ -285,9 +299,11 @@ def main():
         ach = work / (attn_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload) if args.path == "host" else None
     roof["kernel"] = {1: "decode_kernel", 2: "prefill_kernel", 3: "mixed_kernel"}[kind] + \
         " (one launch: KV write, attention, split merge)"
+    if args.path == "graph":
+        roof["kernel"] = "graph replay: graph_kernel (device-planned, persistent)"
     roof["avg_launch_ms"] = round(attn_avg_ms, 5)
 
     cpu = None
@@ -300,7 +316,7 @@ def main():
            "page_size": b.page_size, "pool_pages": b.num_pages, "layout":
            "seq_major" if b.layout == 0 else "kv_head_major", "seed": b.seed,
            "sum_kv_len": int(b.kv_lens.reshape(b.num_seqs, -1)[:, 0].sum()),
-           "cache_flush": args.flush, "parallelism": "none (one GPU)"}
+           "cache_flush": args.flush, "parallelism": "none (one GPU)", "path": args.path}
     if sparse:
         cfg["union_density"] = b.extra["union_density"]
     line = {

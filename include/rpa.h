@@ -134,6 +134,61 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
                          void *stream);
 
 /*
+ * Graph-capturable attention: the same computation as rpa_attention, planned on the
+ * device.  rpa_attention reads the batch's lengths on the host to choose the kernel, the
+ * KV split sizes and the grid; that ties every call to host data and keeps it out of a
+ * captured HIP graph (the ONNX Runtime PR lists graph capture among its deferred items).
+ * Here the host sees only bounds, fixed for the life of a graph.  One persistent kernel,
+ * with a grid that depends only on the device (two workgroups per compute unit), does it
+ * all: every workgroup reads cu_q_lens / kv_lens from device memory and derives the plan
+ * (split sizes, work-item counts) by the host planner's rules, runs its first work item and
+ * then takes items from a queue in the workspace; the last workgroup to finish resets the
+ * queue and advances the split-merge tag kept there.  The launch and its arguments are
+ * identical from call to call, so it can be captured once and replayed with new device
+ * contents.
+ */
+typedef struct rpa_graph_shape {
+  int32_t max_seqs;           /* B_max >= 1: cu_q_lens has B_max + 1 entries, kv_lens B_max
+                                 (x Hkv for HEAD_MAJOR); sequences past the live batch carry
+                                 q_len 0 (repeated cu_q_lens) and are skipped */
+  int32_t max_tokens;         /* T_max >= 1: rows of q, out, k_new, v_new; cu_q_lens[B_max]
+                                 must not exceed it */
+  int32_t max_splits;         /* 1 .. 64: most KV splits of one sequence; the workspace holds
+                                 max_splits partial outputs per row */
+  int32_t num_q_heads;        /* as in rpa_shape */
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t max_pages_per_seq;
+  int32_t layout;
+} rpa_graph_shape;
+
+/* Bytes of workspace rpa_graph_attention needs (plan, queue, split partials and
+ * counters), or (size_t)-1 on an invalid shape.  Unlike rpa_attention's workspace it
+ * carries state from call to call (the split-merge tag): zero it once (any all-zero fill)
+ * before the first call, then keep it for every call with this shape. */
+size_t rpa_graph_workspace_size(const rpa_graph_shape *shape);
+
+/*
+ * rpa_graph_attention -- rpa_attention with device-side planning (see above).
+ *   Arguments as in rpa_attention, with the bounds of *shape in place of the host
+ *   mirrors; q, out, k_new, v_new have max_tokens rows (rows past cu_q_lens[B_max] are
+ *   neither read nor written).  Always one launch on `stream`, also for an empty batch,
+ *   so the call can be captured.  Calls that share a workspace must not overlap (they are
+ *   ordered when made on one stream).
+ * Device data that break the preconditions (a decreasing cu_q_lens, kv_len < q_len, more
+ * blocks than max_pages_per_seq, cu_q_lens[B_max] > max_tokens) make the kernel skip the
+ * whole batch (out and the caches are left untouched) and set the 32-bit status word at
+ * byte offset 0 of the workspace to a non-zero value (0 after a valid batch).
+ */
+rpa_status rpa_graph_attention(const rpa_graph_shape *shape, const void *q, void *k_cache,
+                               void *v_cache, const int32_t *block_tables,
+                               const int32_t *cu_q_lens, const int32_t *kv_lens, float scale,
+                               const void *k_new, const void *v_new, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * rpa_build_union_tables -- per-KV-head block tables of one sequence's chunk
  * from a per-head 2D block mask (CompactAttention, "Core claim" and Figure 3:
  * union over query blocks, then over the query heads of each GQA group).

@@ -158,3 +158,48 @@ def test_union_builder_validation(lib):
     assert lib.rpa_build_union_tables(p, 32, 8, 64, 2048, p, 10, 10, 64, p, p, p, None) == 1
     assert lib.rpa_build_union_tables(p, 32, 8, 64, 16, p, 0, 2000, 64, p, p, p, None) == 1
     assert lib.rpa_build_union_tables(p, 32, 8, 64, 40000, p, 0, 2000, 64, p, p, p, None) == 2
+
+
+def _gshape(**kw):
+    f = dict(max_seqs=4, max_tokens=32, max_splits=8, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             page_size=16, num_pages=64, max_pages_per_seq=16, layout=0)
+    f.update(kw)
+    return _rpa.RpaGraphShape(*[f[n] for n, _ in _rpa.RpaGraphShape._fields_])
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(max_seqs=0), "max_seqs"),
+    (dict(max_tokens=0), "max_tokens"),
+    (dict(max_splits=0), "max_splits"),
+    (dict(max_splits=65), "max_splits"),
+    (dict(num_q_heads=6, num_kv_heads=4), "multiple"),
+    (dict(page_size=24), "page_size"),
+    (dict(page_size=2048), "page_size"),
+    (dict(layout=3), "layout"),
+])
+def test_graph_shape_validation(lib, kw, frag):
+    s = _gshape(**kw)
+    assert lib.rpa_graph_workspace_size(ctypes.byref(s)) == ctypes.c_size_t(-1).value
+    p = ctypes.c_void_p(16)
+    st = lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, 0.1, None, None, p, p, 1 << 30,
+                                 None)
+    assert st == 1 and frag in lib.rpa_last_error().decode()
+
+
+def test_graph_workspace_and_argument_checks(lib):
+    s = _gshape()
+    ws = lib.rpa_graph_workspace_size(ctypes.byref(s))
+    # plan + arguments + 8 splits of fp32 partials for 32 tokens x 8 heads x 128 dims + counters
+    assert ws >= 8 * 32 * 8 * 128 * 4 and ws % 256 == 0
+    s1 = _gshape(max_splits=1)   # no splits: no partials, no counters
+    assert lib.rpa_graph_workspace_size(ctypes.byref(s1)) < 4096
+    p = ctypes.c_void_p(16)
+    assert lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, float("inf"), None, None, p,
+                                   p, ws, None) == 1
+    assert lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, 0.1, p, None, p, p, ws,
+                                   None) == 1
+    assert "both" in lib.rpa_last_error().decode()
+    assert lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, 0.1, None, None, p, None, ws,
+                                   None) == 1
+    assert lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, 0.1, None, None, p, p, ws - 1,
+                                   None) == 3
