@@ -69,6 +69,16 @@ struct AttnArgs {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// The thread index, read once per work item behind an empty asm: values derived from it are
+// then computed per item instead of being hoisted out of a persistent kernel's item loop,
+// where they would hold registers for the whole kernel.
+__device__ __forceinline__ int item_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  __builtin_assume(t >= 0 && t < kThreads);
+  return t;
+}
+
 __device__ __forceinline__ int kv_len_of(const AttnArgs &a, int b, int g) {
   return a.kv_lens[b * a.kvl_seq_stride + g * a.kvl_head_stride];
 }
