@@ -916,20 +916,33 @@ struct PlanScratch {
   long long items[kThreads / 64][2];  // decode, prefill items
 };
 
-__device__ __forceinline__ long long wave_sum64(long long v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Wave-wide reduction of non-negative 32-bit values with DPP moves (no LDS round trips):
+// pairs and quads, then half rows and rows of 16 lanes (every lane then holds its row's
+// result), then rows 1 and 3 take rows 0 and 2 (row broadcast of lane 15) and rows 2 and 3
+// take row 1 (row broadcast of lane 31); lane 63 ends with the whole wave's result.
+template <class Op>
+__device__ __forceinline__ int wave_reduce_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));  // row_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_max32(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+  return wave_reduce_dpp(v, [](int x, int y) { return max(x, y); });
 }
 __device__ __forceinline__ int wave_or32(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off);
-  return v;
+  return wave_reduce_dpp(v, [](int x, int y) { return x | y; });
+}
+// Exact for per-lane values below 2^50: the low 24 bits and the rest are summed apart
+// (64 lanes of 24-bit parts stay below 2^30, of 26-bit parts below 2^32).
+__device__ __forceinline__ long long wave_sum64(long long v) {
+  auto add = [](int x, int y) { return (int)((unsigned)x + (unsigned)y); };
+  const unsigned lo = (unsigned)wave_reduce_dpp((int)(v & 0xffffff), add);
+  const unsigned hi = (unsigned)wave_reduce_dpp((int)(v >> 24), add);
+  return (long long)lo + ((long long)hi << 24);
 }
 
 // The plan of a graph-capturable call, computed by every thread of the workgroup alike.
