@@ -13,6 +13,12 @@ Draw order for every batch, from ``numpy.random.default_rng(seed)``:
   4. q, then k_new, then v_new;
   5. the block mask, for the block-sparse workload.
 
+FP8 caches (``kv_dtype="fp8"``) hold E4M3 codes (``uint8``) drawn directly, not
+quantized from values: sign uniform, exponent field ~ round(N(12, 1.5)) clipped
+to [1, 15], mantissa uniform (the NaN code S.1111.111 becomes S.1111.110), with
+the cache scales ``FP8_SCALE`` = 1/32, so cached values are of order one.  Poisoned
+slots of an FP8 cache hold the NaN code 0x7F.
+
 Named workloads (shapes of Llama-3-8B attention: 32 query heads, 8 KV heads,
 head dim 128) follow the five configurations the path is built for; see
 ``WORKLOADS``.
@@ -28,6 +34,8 @@ SEQ_MAJOR = 0
 HEAD_MAJOR = 1
 
 BF16_NAN = 0x7FC0
+FP8_NAN = 0x7F
+FP8_SCALE = 1.0 / 32.0
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -51,6 +59,21 @@ def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.nd
     return out.reshape(shape)
 
 
+def _fp8_codes(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
+    """E4M3 codes drawn field by field (see the module docstring), in chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        m = e - s
+        sign = rng.integers(0, 2, size=m, dtype=np.uint8)
+        expo = np.clip(np.rint(rng.normal(12.0, 1.5, size=m)), 1, 15).astype(np.uint8)
+        mant = rng.integers(0, 8, size=m, dtype=np.uint8)
+        mant = np.where((expo == 15) & (mant == 7), np.uint8(6), mant)
+        out[s:e] = (sign << 7) | (expo << 3) | mant
+    return out.reshape(shape)
+
+
 @dataclass
 class RaggedBatch:
     name: str
@@ -70,6 +93,12 @@ class RaggedBatch:
     layout: int
     seed: int
     extra: dict = field(default_factory=dict)
+    k_scale: float = 1.0     # FP8 caches: cached K value = code value * k_scale
+    v_scale: float = 1.0
+
+    @property
+    def kv_fp8(self) -> bool:
+        return self.k_cache.dtype == np.uint8
 
     @property
     def num_seqs(self) -> int:
@@ -94,12 +123,13 @@ class RaggedBatch:
 
 def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
                  pool_pages, seed, layout=SEQ_MAJOR, scale=None, max_pages=None, rng=None,
-                 poison_unused=False):
+                 poison_unused=False, kv_dtype="bf16"):
     """A batch of sequences with the given new-token and total lengths.
 
     Pages come from one permutation of ``pool_pages`` physical pages.  With
     ``poison_unused`` every cache slot that no sequence owns (unused pages and
-    the tail slots of each sequence's last page) holds bf16 NaN.  In the
+    the tail slots of each sequence's last page) holds NaN.  ``kv_dtype`` "fp8" gives
+    caches of E4M3 codes with scales FP8_SCALE (drawn in place of the bf16 caches).  In the
     KV-head-major layout ``kv_lens`` may also be given per (sequence, KV head),
     shape [B, Hkv] (each head with its own past, as over compacted tables).
     """
@@ -138,8 +168,11 @@ def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, pag
                 tables[b, g, :nbg] = perm[cur:cur + nbg]
                 cur += nbg
     cache_shape = (pool_pages, S, Hkv, D) if layout == SEQ_MAJOR else (pool_pages, S, D)
-    k_cache = _normal_bf16(rng, cache_shape)
-    v_cache = _normal_bf16(rng, cache_shape)
+    assert kv_dtype in ("bf16", "fp8")
+    fp8 = kv_dtype == "fp8"
+    draw_cache = _fp8_codes if fp8 else _normal_bf16
+    k_cache = draw_cache(rng, cache_shape)
+    v_cache = draw_cache(rng, cache_shape)
     T = int(q_lens.sum())
     q = _normal_bf16(rng, (T, Hq, D))
     k_new = _normal_bf16(rng, (T, Hkv, D))
@@ -159,12 +192,13 @@ def ragged_batch(name, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, pag
                 for i in range((L + S - 1) // S):
                     n = min(S, L - i * S)
                     owned[row[i], :n] = True
-        k_cache[~owned] = BF16_NAN
-        v_cache[~owned] = BF16_NAN
+        k_cache[~owned] = FP8_NAN if fp8 else BF16_NAN
+        v_cache[~owned] = FP8_NAN if fp8 else BF16_NAN
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    cs = FP8_SCALE if fp8 else 1.0
     return RaggedBatch(name, q, k_new, v_new, k_cache, v_cache, tables, cu, kvl, float(scale),
-                       S, Hq, Hkv, D, layout, seed)
+                       S, Hq, Hkv, D, layout, seed, k_scale=cs, v_scale=cs)
 
 
 # --------------------------------------------------------------------------------------
@@ -185,6 +219,13 @@ def llama3_decode(seed=2, num_seqs=64, lo=512, hi=4096, pool_pages=20000, **kw):
                         pool_pages, seed, rng=rng, **kw)
 
 
+def llama3_decode_fp8(seed=2, **kw):
+    """llama3_decode with E4M3 K/V caches (same lengths, pages and queries)."""
+    b = llama3_decode(seed=seed, kv_dtype="fp8", **kw)
+    b.name = "llama3_decode_fp8"
+    return b
+
+
 def llama3_prefill(seed=3, num_seqs=4, seq_len=2048, **kw):
     """4 sequences of 2048 new tokens, no prior context; 32/8/128; page 64."""
     S = 64
@@ -202,6 +243,13 @@ def mixed_chunked(seed=4, chunk=512, context=8192, num_decode=96, lo=1024, hi=81
     kv_lens = np.concatenate([[context + chunk], kv_dec])
     return ragged_batch("mixed_chunked", q_lens, kv_lens, 32, 8, 128, 16, pool_pages, seed,
                         rng=rng, **kw)
+
+
+def mixed_chunked_fp8(seed=4, **kw):
+    """mixed_chunked with E4M3 K/V caches."""
+    b = mixed_chunked(seed=seed, kv_dtype="fp8", **kw)
+    b.name = "mixed_chunked_fp8"
+    return b
 
 
 def block_union_sparse(seed=5, context=131072, chunk=4096, density=0.1, column_shared=False,
@@ -242,4 +290,6 @@ WORKLOADS = {
     "llama3_prefill": llama3_prefill,
     "mixed_chunked": mixed_chunked,
     "block_union_sparse": block_union_sparse,
+    "llama3_decode_fp8": llama3_decode_fp8,
+    "mixed_chunked_fp8": mixed_chunked_fp8,
 }

@@ -12,6 +12,9 @@ Functions (each cites the passage it follows in ``rpa_oracle.c``):
   write_kv        scatter of new K/V rows into their page slots
   attention       page gather + softmax attention, fp64, all rows or sampled rows
   union_tables    Q-block union -> intra-group union -> ascending compaction
+  fp8_encode, fp8_decode
+                  FP8 E4M3 (OCP) codes of a quantized cache; write_kv and attention
+                  take uint8 caches with per-tensor k_scale / v_scale as FP8 caches
 """
 from __future__ import annotations
 
@@ -56,6 +59,17 @@ def _load():
         lib.oracle_attention.restype = i
         lib.oracle_union_tables.argtypes = [p, i, i, i, i, p, i, i, i, p, p, p, p]
         lib.oracle_union_tables.restype = i
+        lib.oracle_write_kv_fp8.argtypes = [i, p, p, i, i, i, i, i, i, p, p, p, p, p,
+                                            ctypes.c_float, ctypes.c_float]
+        lib.oracle_write_kv_fp8.restype = i
+        lib.oracle_attention_fp8.argtypes = [i, p, p, i, i, i, i, i, i, i, p, p, p, p,
+                                             ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                             p, ctypes.c_int64, p, p, i]
+        lib.oracle_attention_fp8.restype = i
+        lib.oracle_fp8_encode.argtypes = [p, p, ctypes.c_int64]
+        lib.oracle_fp8_encode.restype = i
+        lib.oracle_fp8_decode.argtypes = [p, p, ctypes.c_int64]
+        lib.oracle_fp8_decode.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -74,38 +88,67 @@ def num_threads() -> int:
     return _load().oracle_num_threads()
 
 
+def fp8_encode(y):
+    """FP8 E4M3 codes (uint8) of float32 values: clamp to +-448, round to nearest even."""
+    lib = _load()
+    yy = _c(y, np.float32)
+    out = np.zeros(yy.shape, dtype=np.uint8)
+    lib.oracle_fp8_encode(_ptr(yy), _ptr(out), yy.size)
+    return out
+
+
+def fp8_decode(codes):
+    """Values (float64) of FP8 E4M3 codes; the two NaN codes give NaN."""
+    lib = _load()
+    cc = _c(codes, np.uint8)
+    out = np.zeros(cc.shape, dtype=np.float64)
+    lib.oracle_fp8_decode(_ptr(cc), _ptr(out), cc.size)
+    return out
+
+
 def write_kv(cu_q_lens, kv_lens, tables, k_new, v_new, k_cache, v_cache, page_size,
-             layout=SEQ_MAJOR):
-    """Return (k_cache', v_cache'): copies of the caches with the new rows scattered in."""
+             layout=SEQ_MAJOR, k_scale=1.0, v_scale=1.0):
+    """Return (k_cache', v_cache'): copies of the caches with the new rows scattered in.
+
+    uint8 caches are FP8 caches with scales k_scale, v_scale: each new value x is stored
+    as fp8_encode(float32(x) * float32(1 / scale))."""
     lib = _load()
     cu = _c(cu_q_lens, np.int32)
     kl = _c(kv_lens, np.int32)
     tb = _c(tables, np.int32)
     kn = _c(k_new, np.uint16)
     vn = _c(v_new, np.uint16)
-    kc = np.array(k_cache, dtype=np.uint16, copy=True, order="C")
-    vc = np.array(v_cache, dtype=np.uint16, copy=True, order="C")
+    kv8 = np.asarray(k_cache).dtype == np.uint8
+    cdt = np.uint8 if kv8 else np.uint16
+    kc = np.array(k_cache, dtype=cdt, copy=True, order="C")
+    vc = np.array(v_cache, dtype=cdt, copy=True, order="C")
     B = cu.shape[0] - 1
     Hkv, D = kn.shape[1], kn.shape[2]
-    rc = lib.oracle_write_kv(B, _ptr(cu), _ptr(kl), Hkv, D, int(page_size), layout,
-                             tb.shape[-1], kc.shape[0], _ptr(tb), _ptr(kn), _ptr(vn),
-                             _ptr(kc), _ptr(vc))
+    args = (B, _ptr(cu), _ptr(kl), Hkv, D, int(page_size), layout, tb.shape[-1], kc.shape[0],
+            _ptr(tb), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc))
+    if kv8:
+        rc = lib.oracle_write_kv_fp8(*args, float(k_scale), float(v_scale))
+    else:
+        rc = lib.oracle_write_kv(*args)
     if rc != 0:
         raise ValueError(f"oracle_write_kv failed with code {rc}")
     return kc, vc
 
 
 def attention(q, k_cache, v_cache, tables, cu_q_lens, kv_lens, scale, page_size,
-              num_kv_heads, layout=SEQ_MAJOR, block_allowed=None, rows=None, nthreads=0):
+              num_kv_heads, layout=SEQ_MAJOR, block_allowed=None, rows=None, nthreads=0,
+              k_scale=1.0, v_scale=1.0):
     """fp64 attention of every row ([T, Hq, D]) or of sampled rows ([n, D]).
 
     rows: optional int array [n, 2] of (token, query head).
     block_allowed: optional uint8 [B, Hkv, max_pages] restricting visible key blocks.
+    uint8 caches are FP8 caches: a cached K value is fp8_decode(code) * k_scale, V likewise.
     """
     lib = _load()
     qq = _c(q, np.uint16)
-    kc = _c(k_cache, np.uint16)
-    vc = _c(v_cache, np.uint16)
+    kv8 = np.asarray(k_cache).dtype == np.uint8
+    kc = _c(k_cache, np.uint8 if kv8 else np.uint16)
+    vc = _c(v_cache, np.uint8 if kv8 else np.uint16)
     cu = _c(cu_q_lens, np.int32)
     kl = _c(kv_lens, np.int32)
     tb = _c(tables, np.int32)
@@ -119,10 +162,13 @@ def attention(q, k_cache, v_cache, tables, cu_q_lens, kv_lens, scale, page_size,
         rr = _c(rows, np.int32).reshape(-1, 2)
         n = rr.shape[0]
         out = np.zeros((n, D), dtype=np.float64)
-    rc = lib.oracle_attention(B, _ptr(cu), _ptr(kl), Hq, int(num_kv_heads), D, int(page_size),
-                              layout, tb.shape[-1], kc.shape[0], _ptr(tb), _ptr(qq), _ptr(kc),
-                              _ptr(vc), float(scale), _ptr(ba), n, _ptr(rr), _ptr(out),
-                              int(nthreads))
+    head = (B, _ptr(cu), _ptr(kl), Hq, int(num_kv_heads), D, int(page_size), layout,
+            tb.shape[-1], kc.shape[0], _ptr(tb), _ptr(qq), _ptr(kc), _ptr(vc))
+    tail = (_ptr(ba), n, _ptr(rr), _ptr(out), int(nthreads))
+    if kv8:
+        rc = lib.oracle_attention_fp8(*head, float(k_scale), float(v_scale), float(scale), *tail)
+    else:
+        rc = lib.oracle_attention(*head, float(scale), *tail)
     if rc != 0:
         raise ValueError(f"oracle_attention failed with code {rc}")
     return out

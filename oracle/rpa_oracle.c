@@ -21,6 +21,16 @@
  *   oracle_union_tables   Q-block union, then intra-group union, then ascending
  *                         compaction into per-KV-head tables (CompactAttention page,
  *                         "Core claim" and Figure 3; KV-head-major pages, Figure 4).
+ *   oracle_fp8_encode, oracle_fp8_decode, oracle_write_kv_fp8, oracle_attention_fp8
+ *                         the quantized KV cache that the ONNX Runtime PR lists among
+ *                         its deferred items ("Quantized KV cache (T_CACHE)") without
+ *                         fixing a format.  Reading taken here: FP8 E4M3 of the OCP
+ *                         8-bit floating point specification (bias 7, no infinities,
+ *                         S.1111.111 is NaN, largest finite 448), one scale per cache
+ *                         tensor: stored value = code value * scale.  A new K/V value x
+ *                         (bf16) is stored as encode(float(x) * float(1 / scale)), the
+ *                         product and the reciprocal rounded to fp32, the result
+ *                         clamped to +-448 and rounded to nearest, ties to even.
  *
  * Layouts (all row-major):
  *   layout 0, sequence-major:  cache [P][S][Hkv][D]; tables [B][max_pages];
@@ -53,6 +63,69 @@ static double bf16_to_double(uint16_t bits)
     return (double)f;
 }
 
+/* FP8 E4M3 code -> value: exponent field E, mantissa field M; E == 0 is subnormal
+ * (M * 2^-9), otherwise (1 + M/8) * 2^(E-7); E == 15 with M == 7 is NaN. */
+static double fp8_to_double(uint8_t c)
+{
+    int E = (c >> 3) & 15, M = c & 7;
+    double v;
+    if (E == 15 && M == 7)
+        v = NAN;
+    else if (E == 0)
+        v = ldexp((double)M, -9);
+    else
+        v = ldexp(8.0 + M, E - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+/* value -> FP8 E4M3 code, clamped to +-448, rounded to nearest, ties to even.
+ * Every scaling below is by a power of two, hence exact; nearbyint rounds ties to even
+ * in the default rounding mode. */
+static uint8_t fp8_from_float(float y)
+{
+    if (isnan(y))
+        return 0x7F;
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {                 /* subnormal range: steps of 2^-9 */
+        int m = (int)nearbyint(ldexp(a, 9));   /* 0 .. 8; 8 is the smallest normal */
+        return sign | (uint8_t)m;
+    }
+    int e2;
+    frexp(a, &e2);                             /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                            /* a in [2^e, 2^(e+1)) */
+    int r = (int)nearbyint(ldexp(a, 3 - e));   /* 8 .. 16 */
+    if (r == 16) {
+        r = 8;
+        e += 1;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | (r - 8));
+}
+
+int oracle_fp8_encode(const float *y, uint8_t *codes, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = fp8_from_float(y[i]);
+    return 0;
+}
+
+int oracle_fp8_decode(const uint8_t *codes, double *y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = fp8_to_double(codes[i]);
+    return 0;
+}
+
+static float bf16_to_float(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 /* Sequence index b with cu_q_lens[b] <= token < cu_q_lens[b+1] (linear scan). */
 static int seq_of_token(int B, const int32_t *cu_q_lens, int64_t token)
 {
@@ -83,10 +156,12 @@ static int64_t cache_row(int layout, int S, int Hkv, int D, int64_t page, int64_
     return (page * S + slot) * (int64_t)D;
 }
 
-int oracle_write_kv(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
-                    int Hkv, int D, int S, int layout, int max_pages, int num_pages,
-                    const int32_t *tables, const uint16_t *k_new, const uint16_t *v_new,
-                    uint16_t *k_cache, uint16_t *v_cache)
+/* kv8 == 0: caches of bf16, rows copied.  kv8 == 1: caches of FP8 codes, each value
+ * stored as fp8_from_float(float(x) * inv_scale). */
+static int write_kv_impl(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                         int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                         const int32_t *tables, const uint16_t *k_new, const uint16_t *v_new,
+                         void *k_cache, void *v_cache, int kv8, float k_inv, float v_inv)
 {
     if (B < 0 || Hkv <= 0 || D <= 0 || S <= 0 || (layout != 0 && layout != 1))
         return 1;
@@ -109,8 +184,13 @@ int oracle_write_kv(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
                 int64_t dst = cache_row(layout, S, Hkv, D, page, slot, g);
                 int64_t src = ((int64_t)(cu_q_lens[b] + t) * Hkv + g) * D;
                 for (int d = 0; d < D; ++d) {
-                    k_cache[dst + d] = k_new[src + d];
-                    v_cache[dst + d] = v_new[src + d];
+                    if (kv8) {
+                        ((uint8_t *)k_cache)[dst + d] = fp8_from_float(bf16_to_float(k_new[src + d]) * k_inv);
+                        ((uint8_t *)v_cache)[dst + d] = fp8_from_float(bf16_to_float(v_new[src + d]) * v_inv);
+                    } else {
+                        ((uint16_t *)k_cache)[dst + d] = k_new[src + d];
+                        ((uint16_t *)v_cache)[dst + d] = v_new[src + d];
+                    }
                 }
             }
         }
@@ -118,11 +198,41 @@ int oracle_write_kv(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
     return 0;
 }
 
+int oracle_write_kv(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                    int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                    const int32_t *tables, const uint16_t *k_new, const uint16_t *v_new,
+                    uint16_t *k_cache, uint16_t *v_cache)
+{
+    return write_kv_impl(B, cu_q_lens, kv_lens, Hkv, D, S, layout, max_pages, num_pages, tables,
+                         k_new, v_new, k_cache, v_cache, 0, 1.0f, 1.0f);
+}
+
+/* FP8 caches: k_scale, v_scale > 0 are the caches' scales; the reciprocals are taken in fp32. */
+int oracle_write_kv_fp8(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                        int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                        const int32_t *tables, const uint16_t *k_new, const uint16_t *v_new,
+                        uint8_t *k_cache, uint8_t *v_cache, float k_scale, float v_scale)
+{
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f))
+        return 1;
+    return write_kv_impl(B, cu_q_lens, kv_lens, Hkv, D, S, layout, max_pages, num_pages, tables,
+                         k_new, v_new, k_cache, v_cache, 1, 1.0f / k_scale, 1.0f / v_scale);
+}
+
+/* Value d of a cache row: bf16, or FP8 code times the cache's scale. */
+static double cache_value(const void *cache, int kv8, double scale, int64_t idx)
+{
+    if (kv8)
+        return fp8_to_double(((const uint8_t *)cache)[idx]) * scale;
+    return bf16_to_double(((const uint16_t *)cache)[idx]);
+}
+
 /* One query row (token, head): gather, scores, softmax, weighted sum of V. */
 static int attend_row(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
                       int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
-                      const int32_t *tables, const uint16_t *q, const uint16_t *k_cache,
-                      const uint16_t *v_cache, double scale, const uint8_t *block_allowed,
+                      const int32_t *tables, const uint16_t *q, const void *k_cache,
+                      const void *v_cache, int kv8, double k_scale, double v_scale,
+                      double scale, const uint8_t *block_allowed,
                       int64_t token, int h, double *o)
 {
     int b = seq_of_token(B, cu_q_lens, token);
@@ -160,10 +270,10 @@ static int attend_row(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
             rc = 2;
             break;
         }
-        const uint16_t *krow = k_cache + cache_row(layout, S, Hkv, D, page, j % S, g);
+        const int64_t krow = cache_row(layout, S, Hkv, D, page, j % S, g);
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+            dot += bf16_to_double(qrow[d]) * cache_value(k_cache, kv8, k_scale, krow + d);
         score[j] = scale * dot;
         if (score[j] > m)
             m = score[j];
@@ -178,9 +288,9 @@ static int attend_row(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
             double e = exp(score[j] - m);
             l += e;
             int32_t page = table_entry(tables, layout, Hkv, max_pages, b, g, j / S);
-            const uint16_t *vrow = v_cache + cache_row(layout, S, Hkv, D, page, j % S, g);
+            const int64_t vrow = cache_row(layout, S, Hkv, D, page, j % S, g);
             for (int d = 0; d < D; ++d)
-                o[d] += e * bf16_to_double(vrow[d]);
+                o[d] += e * cache_value(v_cache, kv8, v_scale, vrow + d);
         }
         /* l > 0 whenever a key is visible; with none, the row is defined as 0. */
         for (int d = 0; d < D; ++d)
@@ -198,11 +308,12 @@ static int attend_row(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
  * only if its logical block j / S is allowed for the row's KV head.
  * nthreads <= 0 uses the OpenMP default.
  */
-int oracle_attention(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
-                     int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
-                     const int32_t *tables, const uint16_t *q, const uint16_t *k_cache,
-                     const uint16_t *v_cache, double scale, const uint8_t *block_allowed,
-                     int64_t nrows, const int32_t *rows, double *out, int nthreads)
+static int attention_impl(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                          int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                          const int32_t *tables, const uint16_t *q, const void *k_cache,
+                          const void *v_cache, int kv8, double k_scale, double v_scale,
+                          double scale, const uint8_t *block_allowed,
+                          int64_t nrows, const int32_t *rows, double *out, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || S <= 0 ||
         (layout != 0 && layout != 1))
@@ -219,12 +330,36 @@ int oracle_attention(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
         int64_t token = rows ? rows[2 * i] : i / Hq;
         int h = rows ? rows[2 * i + 1] : (int)(i % Hq);
         int r = attend_row(B, cu_q_lens, kv_lens, Hq, Hkv, D, S, layout, max_pages, num_pages,
-                           tables, q, k_cache, v_cache, scale, block_allowed, token, h,
-                           out + i * D);
+                           tables, q, k_cache, v_cache, kv8, k_scale, v_scale, scale,
+                           block_allowed, token, h, out + i * D);
         if (r > rc)
             rc = r;
     }
     return rc;
+}
+
+int oracle_attention(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                     int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                     const int32_t *tables, const uint16_t *q, const uint16_t *k_cache,
+                     const uint16_t *v_cache, double scale, const uint8_t *block_allowed,
+                     int64_t nrows, const int32_t *rows, double *out, int nthreads)
+{
+    return attention_impl(B, cu_q_lens, kv_lens, Hq, Hkv, D, S, layout, max_pages, num_pages,
+                          tables, q, k_cache, v_cache, 0, 1.0, 1.0, scale, block_allowed, nrows,
+                          rows, out, nthreads);
+}
+
+/* The same over FP8 caches: every cached K value is code value * k_scale, V likewise. */
+int oracle_attention_fp8(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                         int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                         const int32_t *tables, const uint16_t *q, const uint8_t *k_cache,
+                         const uint8_t *v_cache, double k_scale, double v_scale, double scale,
+                         const uint8_t *block_allowed, int64_t nrows, const int32_t *rows,
+                         double *out, int nthreads)
+{
+    return attention_impl(B, cu_q_lens, kv_lens, Hq, Hkv, D, S, layout, max_pages, num_pages,
+                          tables, q, k_cache, v_cache, 1, k_scale, v_scale, scale, block_allowed,
+                          nrows, rows, out, nthreads);
 }
 
 int oracle_num_threads(void)

@@ -389,3 +389,104 @@ def test_closed_form_survives_large_scores():
     e = math.e
     expect = np.array([(1 + 3 + 4 * e) / (2 + e), (2 + 5 - 8 * e) / (2 + e)])
     np.testing.assert_allclose(out, expect, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) caches ----
+# The pages leave the quantized cache's format open; the oracle takes OCP FP8 E4M3 with one
+# scale per cache.  torch's float8_e4m3fn is an independent implementation of that format.
+
+def _torch_e4m3(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8_decode_matches_torch():
+    """All 256 codes.  Catches: wrong exponent bias, subnormal scale, sign or NaN pattern."""
+    codes = np.arange(256, dtype=np.uint8)
+    got, ref = oracle.fp8_decode(codes), _torch_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch_in_range():
+    """Random values over the whole range and every midpoint between neighbouring codes.
+    Catches: truncation instead of rounding, ties away from zero, off-by-one exponents at
+    binade edges and in the subnormal range."""
+    rng = np.random.default_rng(8)
+    y = (rng.standard_normal(300000) * np.exp2(rng.integers(-14, 10, 300000))).astype(np.float32)
+    y = y[np.abs(y) <= 448]
+    vals = oracle.fp8_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)   # exact in fp32
+    for x in (y, mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))):
+        ref = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.fp8_encode(x), ref)
+
+
+def test_fp8_encode_saturates_rounds_ties_to_even_and_round_trips():
+    """Out-of-range values clamp to the largest finite code; ties go to the even mantissa;
+    encode(decode(c)) == c for every finite code.  Catches: NaN on overflow, lost -0."""
+    x = np.array([448, 460, 1e9, -1e9, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875],
+                 dtype=np.float32)
+    assert oracle.fp8_encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x02, 0x38, 0x3A]
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert np.array_equal(oracle.fp8_encode(oracle.fp8_decode(codes).astype(np.float32)), codes)
+
+
+@pytest.mark.parametrize("layout", [wl.SEQ_MAJOR, wl.HEAD_MAJOR])
+def test_fp8_write_lands_where_bf16_write_lands(layout):
+    """The FP8 scatter touches exactly the slots the (pinned) bf16 scatter touches, and each
+    stored code is torch's E4M3 of float32(x) * float32(1 / scale).  Catches: a wrong slot or
+    head, the scale applied the wrong way round, rounding before scaling."""
+    b = wl.ragged_batch("w8", [3, 1, 5], [3, 17, 40], 4, 2, 16, 16, 12, 21, layout=layout,
+                        kv_dtype="fp8")
+    ks, vs = 0.37, 1.9
+    k8, v8 = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                             b.k_cache, b.v_cache, b.page_size, layout, k_scale=ks, v_scale=vs)
+    zeros = np.zeros(b.k_cache.shape, np.uint16)
+    kbits, vbits = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                                   zeros, zeros, b.page_size, layout)
+    ones = np.ones_like(b.k_new)   # a non-zero marker in every written slot
+    wmask, _ = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, ones, ones, zeros, zeros,
+                               b.page_size, layout)
+    written = wmask != 0
+    assert np.array_equal(k8[~written], b.k_cache[~written])
+    assert np.array_equal(v8[~written], b.v_cache[~written])
+    inv_k, inv_v = np.float32(1) / np.float32(ks), np.float32(1) / np.float32(vs)
+    kx = (wl.bf16_to_f32(kbits[written]) * inv_k).astype(np.float32)
+    vx = (wl.bf16_to_f32(vbits[written]) * inv_v).astype(np.float32)
+    tk = torch.from_numpy(np.clip(kx, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    tv = torch.from_numpy(np.clip(vx, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(k8[written], tk)
+    assert np.array_equal(v8[written], tv)
+
+
+def _fp8_batch(seed, layout=wl.SEQ_MAJOR):
+    return wl.ragged_batch("a8", [1, 6, 1], [19, 30, 45], 6, 2, 32, 16, 16, seed, layout=layout,
+                           kv_dtype="fp8")
+
+
+@pytest.mark.parametrize("layout", [wl.SEQ_MAJOR, wl.HEAD_MAJOR])
+def test_fp8_attention_equals_bf16_attention_on_exact_values(layout):
+    """With power-of-two scales every dequantized value is exact in bf16, so FP8 attention
+    must equal the pinned bf16 attention over caches holding those values.  Catches: a scale
+    dropped or applied to the wrong cache, codes decoded with the wrong format."""
+    b = _fp8_batch(31, layout)
+    ks, vs = 2.0 ** -3, 2.0
+    got = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_tables, b.cu_q_lens, b.kv_lens,
+                           b.scale, b.page_size, b.num_kv_heads, layout, k_scale=ks, v_scale=vs)
+    kb = wl.bf16_bits((_torch_e4m3(b.k_cache) * ks).astype(np.float32))
+    vb = wl.bf16_bits((_torch_e4m3(b.v_cache) * vs).astype(np.float32))
+    ref = oracle.attention(b.q, kb, vb, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                           b.page_size, b.num_kv_heads, layout)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_attention_scales_are_linear():
+    """k_scale multiplies every score, like the softmax scale; v_scale multiplies the output.
+    Catches: a scale folded into the wrong side, or applied twice."""
+    b = _fp8_batch(32)
+    args = (b.q, b.k_cache, b.v_cache, b.block_tables, b.cu_q_lens, b.kv_lens)
+    base = oracle.attention(*args, b.scale * 0.37, b.page_size, b.num_kv_heads, k_scale=1.0,
+                            v_scale=1.0)
+    got = oracle.attention(*args, b.scale, b.page_size, b.num_kv_heads, k_scale=0.37, v_scale=1.7)
+    np.testing.assert_allclose(got, 1.7 * base, rtol=1e-10, atol=1e-12)
