@@ -8,6 +8,9 @@ CPU fallback: every call fails loudly if the library or a gfx950 device is missi
     attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, ...)
     build_union_tables(mask, base_tables, past, kv_len, page_size)
     GraphAttention(...)   # device-planned call that a HIP graph can capture
+
+Caches are bf16, or FP8 E4M3 codes (uint8 / float8_e4m3fn storage) with per-cache scales
+passed as k_scale / v_scale.
 """
 from ._rpa import (  # noqa: F401
     GraphAttention,
@@ -15,6 +18,8 @@ from ._rpa import (  # noqa: F401
     KERNEL_DECODE,
     KERNEL_MIXED,
     KERNEL_PREFILL,
+    KV_BF16,
+    KV_FP8_E4M3,
     LAYOUT_HEAD_MAJOR,
     LAYOUT_SEQ_MAJOR,
     PreparedAttention,
@@ -22,6 +27,7 @@ from ._rpa import (  # noqa: F401
     RpaError,
     attention,
     build_union_tables,
+    kv_dtype_of,
     library_path,
     load_library,
     select_kernel,

@@ -17,6 +17,8 @@ KERNEL_AUTO = 0
 KERNEL_DECODE = 1
 KERNEL_PREFILL = 2
 KERNEL_MIXED = 3
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librpa.so")
@@ -49,13 +51,17 @@ class RpaShape(ctypes.Structure):
         ("kernel", ctypes.c_int32),
         ("h_cu_q_lens", ctypes.POINTER(ctypes.c_int32)),
         ("h_kv_lens", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
 class RpaGraphShape(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "max_seqs", "max_tokens", "max_splits", "num_q_heads", "num_kv_heads", "head_dim",
-        "page_size", "num_pages", "max_pages_per_seq", "layout")]
+        "page_size", "num_pages", "max_pages_per_seq", "layout", "kv_dtype")] + [
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -121,18 +127,35 @@ def _need_contig(**tensors):
             raise ValueError(f"{name} must be contiguous")
 
 
+def kv_dtype_of(k_cache, v_cache=None):
+    """KV_BF16 for bfloat16 caches, KV_FP8_E4M3 for caches of E4M3 codes (uint8 or
+    torch.float8_e4m3fn storage)."""
+    def one(t):
+        if t.dtype == torch.bfloat16:
+            return KV_BF16
+        if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+            return KV_FP8_E4M3
+        raise ValueError(f"cache dtype {t.dtype}: expected bfloat16, uint8 or float8_e4m3fn")
+    d = one(k_cache)
+    if v_cache is not None and one(v_cache) != d:
+        raise ValueError("k_cache and v_cache must have the same element type")
+    return d
+
+
 class _Shape:
     """An RpaShape plus the host tensors it points into (kept alive with it)."""
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                 max_pages, layout, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+                 max_pages, layout, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO,
+                 kv_dtype=KV_BF16, k_scale=1.0, v_scale=1.0):
         self.cu, cu_p = _host_i32(cu_q_lens_host)
         self.kv, kv_p = _host_i32(kv_lens_host)
         B = self.cu.numel() - 1
         self.c = RpaShape(B, int(self.cu[-1]) if B >= 0 else 0, num_q_heads, num_kv_heads, head_dim,
                           page_size, num_pages, max_pages, layout, kernel,
                           ctypes.cast(cu_p, ctypes.POINTER(ctypes.c_int32)),
-                          ctypes.cast(kv_p, ctypes.POINTER(ctypes.c_int32)))
+                          ctypes.cast(kv_p, ctypes.POINTER(ctypes.c_int32)),
+                          kv_dtype, float(k_scale), float(v_scale))
 
     @property
     def ref(self):
@@ -148,41 +171,46 @@ def _cache_geometry(k_cache, block_tables):
 
 
 def _shape_for(q_heads, k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host, kv_lens_host,
-               kernel):
+               kernel, k_scale=1.0, v_scale=1.0, v_cache=None):
     layout, Hkv, S, D = _cache_geometry(k_cache, block_tables)
     return _Shape(num_q_heads=q_heads, num_kv_heads=Hkv, head_dim=D, page_size=S,
                   num_pages=k_cache.shape[0], max_pages=block_tables.shape[-1], layout=layout,
                   cu_q_lens_host=cu_q_lens if cu_q_lens_host is None else cu_q_lens_host,
-                  kv_lens_host=kv_lens if kv_lens_host is None else kv_lens_host, kernel=kernel)
+                  kv_lens_host=kv_lens if kv_lens_host is None else kv_lens_host, kernel=kernel,
+                  kv_dtype=kv_dtype_of(k_cache, v_cache), k_scale=k_scale, v_scale=v_scale)
 
 
 def write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *,
-             cu_q_lens_host=None, kv_lens_host=None):
-    """Scatter k_new / v_new ([T, Hkv, D] bf16) into the paged caches in place (rpa_write_kv)."""
+             cu_q_lens_host=None, kv_lens_host=None, k_scale=1.0, v_scale=1.0):
+    """Scatter k_new / v_new ([T, Hkv, D] bf16) into the paged caches in place (rpa_write_kv).
+    FP8 caches (uint8 / float8_e4m3fn) store codes with the given scales."""
     lib = load_library()
     _need_contig(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
                  block_tables=block_tables, cu_q_lens=cu_q_lens, kv_lens=kv_lens)
     shape = _shape_for(k_new.shape[1] if k_new.dim() == 3 else 1, k_cache, block_tables, cu_q_lens,
-                       kv_lens, cu_q_lens_host, kv_lens_host, KERNEL_AUTO)
+                       kv_lens, cu_q_lens_host, kv_lens_host, KERNEL_AUTO, k_scale, v_scale,
+                       v_cache)
     _check(lib.rpa_write_kv(shape.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                             _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens),
                             _stream(k_cache.device)))
 
 
-def workspace_size(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+def workspace_size(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO,
+                   k_scale=1.0, v_scale=1.0):
     lib = load_library()
     shape = _shape_for(q.shape[1], k_cache, block_tables, None, None, cu_q_lens_host, kv_lens_host,
-                       kernel)
+                       kernel, k_scale, v_scale)
     n = lib.rpa_attention_workspace_size(shape.ref)
     if n == ctypes.c_size_t(-1).value:
         _check(1)
     return int(n)
 
 
-def select_kernel(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO):
+def select_kernel(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO,
+                  k_scale=1.0, v_scale=1.0):
     lib = load_library()
     shape = _shape_for(q.shape[1], k_cache, block_tables, None, None, cu_q_lens_host, kv_lens_host,
-                       kernel)
+                       kernel, k_scale, v_scale)
     k = lib.rpa_select_kernel(shape.ref)
     if k < 0:
         _check(1)
@@ -191,17 +219,18 @@ def select_kernel(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel
 
 def attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *, k_new=None,
               v_new=None, out=None, workspace=None, cu_q_lens_host=None, kv_lens_host=None,
-              kernel=KERNEL_AUTO):
+              kernel=KERNEL_AUTO, k_scale=1.0, v_scale=1.0):
     """Ragged paged causal GQA attention (rpa_attention); returns out [T, Hq, D] bf16.
 
     cu_q_lens_host / kv_lens_host: CPU int32 mirrors of the device metadata; when omitted
-    they are copied from the device (a synchronising copy).
+    they are copied from the device (a synchronising copy).  FP8 caches (uint8 or
+    float8_e4m3fn storage of E4M3 codes) take their scales k_scale, v_scale.
     """
     lib = load_library()
     _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                  cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
     shape = _shape_for(q.shape[1], k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host,
-                       kv_lens_host, kernel)
+                       kv_lens_host, kernel, k_scale, v_scale, v_cache)
     if out is None:
         out = torch.empty_like(q)
     need = lib.rpa_attention_workspace_size(shape.ref)
@@ -250,12 +279,12 @@ class PreparedAttention:
 
     def __init__(self, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *,
                  k_new=None, v_new=None, out=None, cu_q_lens_host=None, kv_lens_host=None,
-                 kernel=KERNEL_AUTO, workspace=None):
+                 kernel=KERNEL_AUTO, workspace=None, k_scale=1.0, v_scale=1.0):
         self.lib = load_library()
         _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                      cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
         self.shape = _shape_for(q.shape[1], k_cache, block_tables, cu_q_lens, kv_lens,
-                                cu_q_lens_host, kv_lens_host, kernel)
+                                cu_q_lens_host, kv_lens_host, kernel, k_scale, v_scale, v_cache)
         self.out = torch.empty_like(q) if out is None else out
         need = self.lib.rpa_attention_workspace_size(self.shape.ref)
         if need == ctypes.c_size_t(-1).value:
@@ -279,10 +308,11 @@ class PreparedWriteKV:
     """rpa_write_kv with its arguments marshalled once (see PreparedAttention)."""
 
     def __init__(self, k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *,
-                 cu_q_lens_host=None, kv_lens_host=None):
+                 cu_q_lens_host=None, kv_lens_host=None, k_scale=1.0, v_scale=1.0):
         self.lib = load_library()
         self.shape = _shape_for(k_new.shape[1], k_cache, block_tables, cu_q_lens, kv_lens,
-                                cu_q_lens_host, kv_lens_host, KERNEL_AUTO)
+                                cu_q_lens_host, kv_lens_host, KERNEL_AUTO, k_scale, v_scale,
+                                v_cache)
         self.keep = (k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens)
         self.args = (self.shape.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                      _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens), _stream(k_cache.device))
@@ -302,13 +332,14 @@ class GraphAttention:
     """
 
     def __init__(self, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *,
-                 k_new=None, v_new=None, out=None, max_splits=16):
+                 k_new=None, v_new=None, out=None, max_splits=16, k_scale=1.0, v_scale=1.0):
         self.lib = load_library()
         _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                      cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
         layout, Hkv, S, D = _cache_geometry(k_cache, block_tables)
         self.shape = RpaGraphShape(cu_q_lens.numel() - 1, q.shape[0], max_splits, q.shape[1], Hkv,
-                                   D, S, k_cache.shape[0], block_tables.shape[-1], layout)
+                                   D, S, k_cache.shape[0], block_tables.shape[-1], layout,
+                                   kv_dtype_of(k_cache, v_cache), float(k_scale), float(v_scale))
         need = self.lib.rpa_graph_workspace_size(ctypes.byref(self.shape))
         if need == ctypes.c_size_t(-1).value:
             _check(1)

@@ -125,7 +125,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int tok
     }
     M = Mn;
   }
-  const float inv = 1.f / L;
+  const float inv = a.out_scale / L;
   uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
 #pragma unroll
   for (int q = 0; q < NPT / 4; ++q)
@@ -175,20 +175,24 @@ __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
   return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits_dec(a, b);
 }
 
-template <int D>
+template <int D, bool KV8>
 __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   constexpr int KK = D / 32;     // 16x16x32 MFMAs per chunk for QK^T; load instructions per chunk
   constexpr int MB = D / 16;     // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
   constexpr int LPR = D / 8;     // lanes per 16-key row when loading
   constexpr int RPI = 64 / LPR;  // rows per load instruction
+  // FP8 cache: a lane loads 16 codes (16 bytes) of a row; new keys come as 32 bytes of bf16.
+  constexpr int LPR8 = D / 16;     // lanes per row
+  constexpr int RPI8 = 64 / LPR8;  // rows per load instruction
+  constexpr int NI8 = 16 / RPI8;   // load instructions per 16-key chunk (registers: 2 per)
   DecodeSmem<D> &sm = *reinterpret_cast<DecodeSmem<D> *>(smem_raw);
   const int tid = item_tid();
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15;
   const int j = lane >> 4;
-  const int lrow = lane / LPR;
-  const int lchk = lane % LPR;
+  const int lrow = KV8 ? lane / LPR8 : lane / LPR;
+  const int lchk = KV8 ? lane % LPR8 : lane % LPR;
 
   const ItemRef it = find_item(id, a.B, [&](int b) { return decode_count(a, b); });
   const int b = __builtin_amdgcn_readfirstlane(it.b);
@@ -242,9 +246,32 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
 
   // Chunk i of this wave holds keys key0 .. key0+15 (one page: pages hold >= 16 keys); load
   // instruction t brings rows lrow + RPI*t.  Rows of new keys come from k_new / v_new.
+  const uint8_t *const k8 = reinterpret_cast<const uint8_t *>(a.k_cache);
+  const uint8_t *const v8 = reinterpret_cast<const uint8_t *>(a.v_cache);
   auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
     const int page = __builtin_amdgcn_readlane(pg_lane, i);
+    if constexpr (KV8) {
+      // registers 2t, 2t+1: the row's codes (cached key) or its 16 bf16 values (new key)
+#pragma unroll
+      for (int t = 0; t < NI8; ++t) {
+        const int r = lrow + RPI8 * t;
+        const int key = key0 + r;
+        if (fused && key >= past) {
+          // keys past the sequence's end (the chunk's tail) read its last new row instead
+          const int64_t noff = ((int64_t)(q0 + min(key, kv_len - 1) - past) * a.Hkv + g) * D + 16 * lchk;
+          kr[2 * t] = *reinterpret_cast<const u32x4 *>(a.k_new + noff);
+          kr[2 * t + 1] = *reinterpret_cast<const u32x4 *>(a.k_new + noff + 8);
+          vr[2 * t] = *reinterpret_cast<const u32x4 *>(a.v_new + noff);
+          vr[2 * t + 1] = *reinterpret_cast<const u32x4 *>(a.v_new + noff + 8);
+        } else {
+          const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
+          kr[2 * t] = *reinterpret_cast<const u32x4 *>(k8 + coff);
+          vr[2 * t] = *reinterpret_cast<const u32x4 *>(v8 + coff);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < KK; ++t) {
       const int r = lrow + RPI * t;
@@ -253,7 +280,8 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
       const uint16_t *kp = a.k_cache + coff;
       const uint16_t *vp = a.v_cache + coff;
       if (fused && key >= past) {
-        const int64_t noff = ((int64_t)(q0 + key - past) * a.Hkv + g) * D + 8 * lchk;
+        // keys past the sequence's end (the chunk's tail) read its last new row instead
+        const int64_t noff = ((int64_t)(q0 + min(key, kv_len - 1) - past) * a.Hkv + g) * D + 8 * lchk;
         kp = a.k_new + noff;
         vp = a.v_new + noff;
       }
@@ -266,6 +294,33 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
     const int page = __builtin_amdgcn_readlane(pg_lane, i);
     // Stage in LDS (V rows of keys past the item's range are zeroed: they may hold anything);
     // the writer item also stores the new keys into their page slots.
+    if constexpr (KV8) {
+      // New keys are quantized here exactly as the cache stores them, so every reader sees
+      // the stored codes; LDS holds the codes' bf16 values in the bf16 layout.
+#pragma unroll
+      for (int t = 0; t < NI8; ++t) {
+        const int r = lrow + RPI8 * t;
+        const int key = key0 + r;
+        u32x4 kc = kr[2 * t], vc = vr[2 * t];
+        if (fused && key >= past) {
+          kc = quantize16(kr[2 * t], kr[2 * t + 1], a.k_inv);
+          vc = quantize16(vr[2 * t], vr[2 * t + 1], a.v_inv);
+          if (writer && key < k_end) {
+            const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
+            *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(k8) + coff) = kc;
+            *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(v8) + coff) = vc;
+          }
+        }
+        if (key >= k_end) vc = u32x4{0u, 0u, 0u, 0u};
+        u32x4 lo, hi;
+        dequant16(kc, lo, hi);
+        *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, 2 * lchk)) = lo;
+        *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, 2 * lchk + 1)) = hi;
+        dequant16(vc, lo, hi);
+        *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk)) = lo;
+        *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk + 1)) = hi;
+      }
+    } else {
 #pragma unroll
     for (int t = 0; t < KK; ++t) {
       const int r = lrow + RPI * t;
@@ -277,6 +332,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + coff) = kr[t];
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + coff) = vr[t];
       }
+    }
     }
     // S^T = K Q^T: lane (r16, j) takes K row r16, dims 32kk + 8j .. +8 as its A operand.
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
@@ -381,7 +437,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   const int h = g * a.G + frow % a.G;
   if (nsplit == 1) {
     if (!out_ok) return;
-    const float inv = 1.f / L;
+    const float inv = a.out_scale / L;
     uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
 #pragma unroll
     for (int q = 0; q < DPT / 4; ++q)
@@ -440,7 +496,7 @@ __device__ __forceinline__ int prefill_count(const AttnArgs &a, int b) {
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-template <int D>
+template <int D, bool KV8>
 __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, int *last_flag) {
   constexpr int KS = D / 16;                                // QK^T MFMAs per 32-key block
   constexpr int MD = D / 32;                                // PV output blocks of 32 dims
@@ -617,6 +673,69 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     }
   };
 
+  // FP8 cache: tiles go through registers instead (codes, or the bf16 values of new keys),
+  // and are written to LDS as the codes' bf16 values in the bf16 layout.  Wave w, round u
+  // takes rows RPW8 (4u + w) .. + RPW8 - 1 of the tile (one page: RPW8 <= 16 and aligned),
+  // lane l 16 values of row l / LPR8.
+  constexpr int LPR8 = D / 16;                     // lanes per row
+  constexpr int RPW8 = 64 / LPR8;                  // rows per wave per round
+  constexpr int NR8 = kPrefillKeys / (4 * RPW8);   // rounds per tile
+  const int lr8 = lane / LPR8;
+  const int c16 = lane % LPR8;
+  const uint8_t *const kc8 = reinterpret_cast<const uint8_t *>(a.k_cache) + (int64_t)g * a.head_stride;
+  const uint8_t *const vc8 = reinterpret_cast<const uint8_t *>(a.v_cache) + (int64_t)g * a.head_stride;
+  u32x4 kst[2 * NR8], vst[2 * NR8];
+  auto load8 = [&](int tile) {
+    const int kt0 = k_begin + tile * kPrefillKeys;
+    const int last_blk = (min(kt0 + kPrefillKeys, k_end) - 1) >> a.page_shift;
+    if (last_blk - pg_blk0 >= 64) fetch_pages(kt0 >> a.page_shift);
+#pragma unroll
+    for (int u = 0; u < NR8; ++u) {
+      const int g0 = min(kt0 + RPW8 * (4 * u + w), k_end - 1);  // rows past the range repeat
+      const int key = min(g0 + lr8, k_end - 1);                  // the range's last key
+      if (fused && key >= past) {
+        const int64_t noff = new_row0 + (int64_t)key * new_stride + 16 * c16;
+        kst[2 * u] = *reinterpret_cast<const u32x4 *>(a.k_new + noff);
+        kst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(a.k_new + noff + 8);
+        vst[2 * u] = *reinterpret_cast<const u32x4 *>(a.v_new + noff);
+        vst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(a.v_new + noff + 8);
+      } else {
+        const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+        const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
+        kst[2 * u] = *reinterpret_cast<const u32x4 *>(kc8 + off);
+        vst[2 * u] = *reinterpret_cast<const u32x4 *>(vc8 + off);
+      }
+    }
+  };
+  auto commit8 = [&](int tile, auto par) {
+    constexpr int buf = decltype(par)::value;
+    const int kt0 = k_begin + tile * kPrefillKeys;
+#pragma unroll
+    for (int u = 0; u < NR8; ++u) {
+      const int row = RPW8 * (4 * u + w) + lr8;  // row within the tile
+      const int g0 = min(kt0 + RPW8 * (4 * u + w), k_end - 1);
+      const int key = min(kt0 + row, k_end - 1);
+      u32x4 kc = kst[2 * u], vc = vst[2 * u];
+      if (fused && key >= past) {
+        kc = quantize16(kst[2 * u], kst[2 * u + 1], a.k_inv);
+        vc = quantize16(vst[2 * u], vst[2 * u + 1], a.v_inv);
+        if (writer && kt0 + row < k_end) {  // the item owning the last query rows stores them
+          const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+          const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
+          *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(kc8) + off) = kc;
+          *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(vc8) + off) = vc;
+        }
+      }
+      u32x4 lo, hi;
+      dequant16(kc, lo, hi);
+      *reinterpret_cast<u32x4 *>(kbuf[buf] + lds_off<D>(row, 2 * c16)) = lo;
+      *reinterpret_cast<u32x4 *>(kbuf[buf] + lds_off<D>(row, 2 * c16 + 1)) = hi;
+      dequant16(vc, lo, hi);
+      *reinterpret_cast<u32x4 *>(vbuf[buf] + lds_off<D>(row, 2 * c16)) = lo;
+      *reinterpret_cast<u32x4 *>(vbuf[buf] + lds_off<D>(row, 2 * c16 + 1)) = hi;
+    }
+  };
+
   // LDS read addresses that do not change from tile to tile (bytes).
   const int k_rd_base = lds_off<D>(r32, hf) * 2;
   const int i16 = lane & 15;
@@ -742,17 +861,32 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   // buffers' accesses apart for the compiler.
   auto step = [&](int tile, auto par, auto masked) {
     constexpr int P = decltype(par)::value;
-    if (writer) write_new_rows(tile, par);
-    if (tile + 1 < n_tiles) issue_tile(tile + 1, std::integral_constant<int, 1 - P>{});
-    compute_tile(tile, par, masked);
-    wait_all_memory();
-    __syncthreads();
+    if constexpr (KV8) {
+      // FP8: tile i+1's loads are in flight in registers while tile i is computed, then
+      // they are converted into the other buffer.
+      const bool more = tile + 1 < n_tiles;
+      if (more) load8(tile + 1);
+      compute_tile(tile, par, masked);
+      if (more) commit8(tile + 1, std::integral_constant<int, 1 - P>{});
+      __syncthreads();
+    } else {
+      if (writer) write_new_rows(tile, par);
+      if (tile + 1 < n_tiles) issue_tile(tile + 1, std::integral_constant<int, 1 - P>{});
+      compute_tile(tile, par, masked);
+      wait_all_memory();
+      __syncthreads();
+    }
   };
   using even = std::integral_constant<int, 0>;
   using odd = std::integral_constant<int, 1>;
   if (n_tiles > 0) {
     fetch_pages(blk_begin);
-    issue_tile(0, even{});
+    if constexpr (KV8) {
+      load8(0);
+      commit8(0, even{});
+    } else {
+      issue_tile(0, even{});
+    }
   }
   // Nothing the prologue loaded (Q, tile 0) may still be in flight inside the loop: a wait
   // there would also wait for the next tile's loads.
@@ -773,7 +907,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   const int token = q0 + t_row;
   if (nsplit == 1) {
     if (!row_ok) return;
-    const float inv = 1.f / l_run;
+    const float inv = a.out_scale / l_run;
     uint16_t *op = a.out + ((int64_t)token * a.Hq + h_row) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
@@ -822,21 +956,21 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
 
 // =========================================================================== kernels ======
 
-template <int D>
 #ifndef RPA_DECODE_MIN_BLOCKS
 #define RPA_DECODE_MIN_BLOCKS 2
 #endif
+template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
-  decode_item<D>(a, blockIdx.x, smem);
+  decode_item<D, KV8>(a, blockIdx.x, smem);
 }
 
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds0[kPrefillBufBytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
   __shared__ int last;
-  prefill_item<D>(a, blockIdx.x, lds0, lds1, &last);
+  prefill_item<D, KV8>(a, blockIdx.x, lds0, lds1, &last);
 }
 
 // One launch for a batch holding both kinds: prefill items first (they are the longest),
@@ -845,31 +979,31 @@ template <int D>
 constexpr size_t kMixedLds0Bytes =
     sizeof(DecodeSmem<D>) > (size_t)kPrefillBufBytes<D> ? sizeof(DecodeSmem<D>) : kPrefillBufBytes<D>;
 
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
   __shared__ int last;
   if ((int)blockIdx.x < a.n_pf_items)
-    prefill_item<D>(a, blockIdx.x, lds0, lds1, &last);
+    prefill_item<D, KV8>(a, blockIdx.x, lds0, lds1, &last);
   else
-    decode_item<D>(a, blockIdx.x - a.n_pf_items, lds0);
+    decode_item<D, KV8>(a, blockIdx.x - a.n_pf_items, lds0);
 }
 
-template <int D>
+template <int D, bool KV8>
 static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_blocks,
                                      hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_blocks), block(kThreads);
   switch (kind) {
     case AttnKernel::kDecode:
-      hipLaunchKernelGGL(decode_kernel<D>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<D, KV8>), grid, block, 0, stream, a);
       break;
     case AttnKernel::kPrefill:
-      hipLaunchKernelGGL(prefill_kernel<D>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<D, KV8>), grid, block, 0, stream, a);
       break;
     case AttnKernel::kMixed:
-      hipLaunchKernelGGL(mixed_kernel<D>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((mixed_kernel<D, KV8>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -877,8 +1011,11 @@ static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_b
 
 hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
                             hipStream_t stream) {
-  if (D == 128) return launch_attention_d<128>(a, kind, n_blocks, stream);
-  return launch_attention_d<64>(a, kind, n_blocks, stream);
+  if (D == 128)
+    return a.kv8 ? launch_attention_d<128, true>(a, kind, n_blocks, stream)
+                 : launch_attention_d<128, false>(a, kind, n_blocks, stream);
+  return a.kv8 ? launch_attention_d<64, true>(a, kind, n_blocks, stream)
+               : launch_attention_d<64, false>(a, kind, n_blocks, stream);
 }
 
 }  // namespace rpa
@@ -1056,7 +1193,7 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
 }
 
 // Persistent attention: items run exactly as in the mixed kernel (prefill items first).
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, GraphPlanArgs p) {
   __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
@@ -1089,16 +1226,16 @@ __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, Graph
   // to that kind (a shared loop measured ~20% slower per decode item).
   if (c.n_pf_items == 0) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
-      decode_item<D>(a, item, lds0);
+      decode_item<D, KV8>(a, item, lds0);
   } else if (c.n_pf_items == c.n_items) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
-      prefill_item<D>(a, item, lds0, lds1, &last);
+      prefill_item<D, KV8>(a, item, lds0, lds1, &last);
   } else {
     for (int item = blockIdx.x; item < c.n_items; item = next_item()) {
       if (item < c.n_pf_items)
-        prefill_item<D>(a, item, lds0, lds1, &last);
+        prefill_item<D, KV8>(a, item, lds0, lds1, &last);
       else
-        decode_item<D>(a, item - c.n_pf_items, lds0);
+        decode_item<D, KV8>(a, item - c.n_pf_items, lds0);
     }
   }
   // Leaving: the queue and tag accesses of this workgroup are complete (their values were
@@ -1119,9 +1256,11 @@ hipError_t launch_graph_attention(const AttnArgs &a, const GraphPlanArgs &p, int
                                   int n_workgroups, hipStream_t stream) {
   const dim3 grid((unsigned)n_workgroups), block(kThreads);
   if (D == 128)
-    hipLaunchKernelGGL(graph_kernel<128>, grid, block, 0, stream, a, p);
+    hipLaunchKernelGGL((a.kv8 ? graph_kernel<128, true> : graph_kernel<128, false>), grid, block, 0,
+                       stream, a, p);
   else
-    hipLaunchKernelGGL(graph_kernel<64>, grid, block, 0, stream, a, p);
+    hipLaunchKernelGGL((a.kv8 ? graph_kernel<64, true> : graph_kernel<64, false>), grid, block, 0,
+                       stream, a, p);
   return hipGetLastError();
 }
 

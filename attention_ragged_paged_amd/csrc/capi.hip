@@ -93,6 +93,27 @@ int max_kv_len_host(const rpa_shape *s, int b) {
   return m;
 }
 
+rpa_status validate_kv_dtype(int32_t kv_dtype, float k_scale, float v_scale) {
+  if (kv_dtype != RPA_KV_BF16 && kv_dtype != RPA_KV_FP8_E4M3)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "kv_dtype %d is not a RPA_KV_* value", kv_dtype);
+  if (kv_dtype == RPA_KV_FP8_E4M3 &&
+      !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f &&
+        std::isfinite(1.f / k_scale) && std::isfinite(1.f / v_scale)))
+    return fail(RPA_ERR_INVALID_ARGUMENT,
+                "FP8 cache scales k_scale %g and v_scale %g must be finite and > 0 (with finite "
+                "reciprocals)", (double)k_scale, (double)v_scale);
+  return RPA_OK;
+}
+
+// Fields of the kernels' arguments that depend on the cache type.
+template <class Args>
+void fill_kv_dtype(Args &a, int32_t kv_dtype, float k_scale, float v_scale) {
+  const bool kv8 = kv_dtype == RPA_KV_FP8_E4M3;
+  a.kv8 = kv8 ? 1 : 0;
+  a.k_inv = kv8 ? 1.f / k_scale : 1.f;
+  a.v_inv = kv8 ? 1.f / v_scale : 1.f;
+}
+
 rpa_status validate(const rpa_shape *s, bool need_lens) {
   if (!s) return fail(RPA_ERR_INVALID_ARGUMENT, "shape is NULL");
   if (s->num_seqs < 0) return fail(RPA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", s->num_seqs);
@@ -121,6 +142,10 @@ rpa_status validate(const rpa_shape *s, bool need_lens) {
     return fail(RPA_ERR_INVALID_ARGUMENT, "layout %d unknown", s->layout);
   if (s->kernel < RPA_KERNEL_AUTO || s->kernel > RPA_KERNEL_MIXED)
     return fail(RPA_ERR_INVALID_ARGUMENT, "kernel %d unknown", s->kernel);
+  {
+    const rpa_status st = validate_kv_dtype(s->kv_dtype, s->k_scale, s->v_scale);
+    if (st != RPA_OK) return st;
+  }
   if (!need_lens) return RPA_OK;
   if (!s->h_cu_q_lens || (s->num_seqs > 0 && !s->h_kv_lens))
     return fail(RPA_ERR_INVALID_ARGUMENT, "host mirrors of cu_q_lens / kv_lens are NULL");
@@ -323,6 +348,7 @@ rpa_status write_kv_impl(const rpa_shape *s, const void *k_new, const void *v_ne
   w.page_shift = ilog2(s->page_size);
   fill_layout(s, w.page_stride, w.slot_stride, w.head_stride, w.bt_seq_stride, w.bt_head_stride,
               w.kvl_seq_stride, w.kvl_head_stride);
+  fill_kv_dtype(w, s->kv_dtype, s->k_scale, s->v_scale);
   hipError_t e = rpa::launch_write_kv(w, s->head_dim, stream);
   if (e != hipSuccess) return fail(RPA_ERR_HIP, "write_kv launch: %s", hipGetErrorString(e));
   return RPA_OK;
@@ -405,7 +431,10 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   a.page_shift = ilog2(shape->page_size);
   fill_layout(shape, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride,
               a.bt_head_stride, a.kvl_seq_stride, a.kvl_head_stride);
-  a.scale_log2 = scale * 1.4426950408889634f;
+  fill_kv_dtype(a, shape->kv_dtype, shape->k_scale, shape->v_scale);
+  // FP8 caches hold code values: K's scale joins the softmax scale, V's the output.
+  a.scale_log2 = scale * 1.4426950408889634f * (a.kv8 ? shape->k_scale : 1.f);
+  a.out_scale = a.kv8 ? shape->v_scale : 1.f;
   a.dec_rows_max = p.dec_rows_max;
   a.split_dec = p.split_dec;
   a.split_pf = p.split_pf;
@@ -448,7 +477,7 @@ rpa_status validate_graph(const rpa_graph_shape *s) {
                 s->num_pages, s->max_pages_per_seq);
   if (s->layout != RPA_LAYOUT_SEQ_MAJOR && s->layout != RPA_LAYOUT_HEAD_MAJOR)
     return fail(RPA_ERR_INVALID_ARGUMENT, "layout %d is not a RPA_LAYOUT_* value", s->layout);
-  return RPA_OK;
+  return validate_kv_dtype(s->kv_dtype, s->k_scale, s->v_scale);
 }
 
 // Graph workspace: [plan][split partials, (m, l) pairs, counters].
@@ -552,7 +581,9 @@ rpa_status rpa_graph_attention(const rpa_graph_shape *shape, const void *q, void
   a.page_shift = ilog2(shape->page_size);
   fill_layout(&s, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride, a.bt_head_stride,
               a.kvl_seq_stride, a.kvl_head_stride);
-  a.scale_log2 = scale * 1.4426950408889634f;
+  fill_kv_dtype(a, shape->kv_dtype, shape->k_scale, shape->v_scale);
+  a.scale_log2 = scale * 1.4426950408889634f * (a.kv8 ? shape->k_scale : 1.f);
+  a.out_scale = a.kv8 ? shape->v_scale : 1.f;
   a.dec_rows_max = kDecodeRowsMax;
   a.pf_tokens = std::max(1, rpa::kPrefillRows / a.G);
   a.pf_counter_base = (int32_t)gl.pf_counter_base;

@@ -58,7 +58,10 @@ struct AttnArgs {
   int64_t page_stride, slot_stride, head_stride;  // cache element strides
   int32_t bt_seq_stride, bt_head_stride;          // table entry (b, g, i) = tables[b*seq + g*head + i]
   int32_t kvl_seq_stride, kvl_head_stride;        // kv_len(b, g) = kv_lens[b*seq + g*head]
-  float scale_log2;         // softmax scale * log2(e)
+  float scale_log2;         // softmax scale * log2(e) (* k_scale for an FP8 cache)
+  float out_scale;          // multiplies every output: 1, or v_scale for an FP8 cache
+  float k_inv, v_inv;       // FP8 cache: 1 / k_scale, 1 / v_scale (fp32), for new K/V
+  int32_t kv8;              // caches of FP8 E4M3 codes (selects the kernels' FP8 variants)
   int32_t dec_rows_max;     // a sequence is decode-class iff q_len * G <= dec_rows_max
   int32_t split_dec;        // keys per split of a decode-class sequence (multiple of 64)
   int32_t split_pf;         // keys per split of a prefill-class sequence (multiple of 64)
@@ -174,6 +177,44 @@ __device__ __forceinline__ int swz_chunk(int r, int c) {
 template <int D>
 __device__ __forceinline__ int lds_off(int r, int c) {  // offset in bf16 elements
   return r * D + swz_chunk<D>(r, c) * 8;
+}
+
+// FP8 E4M3 (the OCP format: bias 7, no infinities, largest finite 448) for quantized caches.
+// A new value x is stored as the code of x * inv_scale, clamped to +-448 and rounded to
+// nearest even (v_cvt_pk_fp8_f32); codes are read back exactly as bf16 code values
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16 value), and the
+// caches' scales are applied to the scores and to the output instead.
+__device__ __forceinline__ float fp8_clamp(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+
+// 8 bf16 values (u32x4) -> 8 codes (u32x2), element i in byte i.
+__device__ __forceinline__ u32x2 quantize8(const u32x4 &v, float inv) {
+  u32x2 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t w0 = v[2 * i], w1 = v[2 * i + 1];
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(bf16_lo(w0) * inv), fp8_clamp(bf16_hi(w0) * inv), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(bf16_lo(w1) * inv), fp8_clamp(bf16_hi(w1) * inv), c, true);
+    r[i] = (uint32_t)c;
+  }
+  return r;
+}
+
+// 16 bf16 values (lo: elements 0..7, hi: 8..15) -> 16 codes.
+__device__ __forceinline__ u32x4 quantize16(const u32x4 &lo, const u32x4 &hi, float inv) {
+  const u32x2 a = quantize8(lo, inv), b = quantize8(hi, inv);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// 16 codes -> 16 bf16 code values (lo: elements 0..7, hi: 8..15), exact.
+__device__ __forceinline__ void dequant16(const u32x4 &c, u32x4 &lo, u32x4 &hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[i], 1.0f, false));
+    w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[i], 1.0f, true));
+  }
+  lo = u32x4{w[0], w[1], w[2], w[3]};
+  hi = u32x4{w[4], w[5], w[6], w[7]};
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i

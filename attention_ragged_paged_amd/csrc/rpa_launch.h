@@ -21,6 +21,8 @@ struct WriteArgs {
   int64_t page_stride, slot_stride, head_stride;
   int32_t bt_seq_stride, bt_head_stride;
   int32_t kvl_seq_stride, kvl_head_stride;
+  int32_t kv8;               // caches of FP8 E4M3 codes (else bf16)
+  float k_inv, v_inv;        // FP8: 1 / k_scale, 1 / v_scale
 };
 
 enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };

@@ -5,7 +5,8 @@
 // token, page = block_table[position / page_size], slot = position % page_size.  Unlike
 // that program (one invocation per element, linear scan for the sequence), one thread
 // here moves a 16-byte chunk, so a wave moves whole 256-byte rows (D = 128) and every
-// store is a full, aligned row segment; the sequence comes from a binary search.
+// store is a full, aligned row segment; the sequence comes from a binary search.  An FP8
+// cache stores each value as the E4M3 code of x / scale (see quantize8), 8 bytes a thread.
 #include "rpa_device.h"
 #include "rpa_launch.h"
 
@@ -25,7 +26,7 @@ __device__ __forceinline__ int seq_of_token(const int32_t *cu_q_lens, int B, int
   return lo;
 }
 
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   constexpr int kChunks = D / 8;  // 16-byte chunks per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -46,8 +47,13 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   const int64_t src = row * D + c * 8;
   const u32x4 kv = *reinterpret_cast<const u32x4 *>(a.k_new + src);
   const u32x4 vv = *reinterpret_cast<const u32x4 *>(a.v_new + src);
-  *reinterpret_cast<u32x4 *>(a.k_cache + dst) = kv;
-  *reinterpret_cast<u32x4 *>(a.v_cache + dst) = vv;
+  if constexpr (KV8) {
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(a.k_cache) + dst) = quantize8(kv, a.k_inv);
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(a.v_cache) + dst) = quantize8(vv, a.v_inv);
+  } else {
+    *reinterpret_cast<u32x4 *>(a.k_cache + dst) = kv;
+    *reinterpret_cast<u32x4 *>(a.v_cache + dst) = vv;
+  }
 }
 
 hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream) {
@@ -55,9 +61,11 @@ hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream) {
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (blocks == 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL(write_kv_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((a.kv8 ? write_kv_kernel<128, true> : write_kv_kernel<128, false>), dim3(blocks),
+                       dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(write_kv_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((a.kv8 ? write_kv_kernel<64, true> : write_kv_kernel<64, false>), dim3(blocks),
+                       dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

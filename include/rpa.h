@@ -69,6 +69,18 @@ enum { RPA_LAYOUT_SEQ_MAJOR = 0, RPA_LAYOUT_HEAD_MAJOR = 1 };
  * kinds exist for cross-checks; each kernel is correct for any batch. */
 enum { RPA_KERNEL_AUTO = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_PREFILL = 2, RPA_KERNEL_MIXED = 3 };
 
+/* Cache element types.  The ONNX Runtime PR defers a quantized KV cache ("Quantized
+ * KV cache (T_CACHE)") without fixing a format; the one built here is:
+ *   BF16      caches of bf16 values (2 bytes an element).
+ *   FP8_E4M3  caches of 1-byte codes in the OCP FP8 E4M3 format (bias 7, no
+ *             infinities, largest finite 448, S.1111.111 NaN) with one scale per
+ *             cache: a cached K value is code value * k_scale, a V value code
+ *             value * v_scale.  A new value x is stored as the code of
+ *             float(x) * float(1 / scale) clamped to +-448, rounded to nearest
+ *             even; attention over new keys sees those stored codes.  Element
+ *             strides are those of the bf16 layouts, in bytes. */
+enum { RPA_KV_BF16 = 0, RPA_KV_FP8_E4M3 = 1 };
+
 typedef struct rpa_shape {
   int32_t num_seqs;           /* B >= 0 */
   int32_t total_q;            /* T = cu_q_lens[B] */
@@ -82,6 +94,8 @@ typedef struct rpa_shape {
   int32_t kernel;             /* RPA_KERNEL_* (AUTO in normal use) */
   const int32_t *h_cu_q_lens; /* host mirror of cu_q_lens, [B + 1] */
   const int32_t *h_kv_lens;   /* host mirror of kv_lens, [B] or [B][Hkv] */
+  int32_t kv_dtype;           /* RPA_KV_*: element type of k_cache and v_cache */
+  float k_scale, v_scale;     /* FP8_E4M3: the caches' scales (finite, > 0); else ignored */
 } rpa_shape;
 
 /*
@@ -91,10 +105,12 @@ typedef struct rpa_shape {
  * page = table(b, g)[pos / page_size], slot = pos % page_size, and the D values
  * of k_new[cu_q_lens[b] + t][g] (likewise v_new) are copied into that slot.
  *   k_new, v_new  device bf16 [T][Hkv][D]
- *   k_cache, v_cache  device bf16, layout per shape->layout, written in place
+ *   k_cache, v_cache  device caches of shape->kv_dtype, layout per shape->layout,
+ *                 written in place
  *   block_tables, cu_q_lens, kv_lens  device int32 copies of the table and of
  *                 the host mirrors in *shape
- * Bit-exact copy; no other cache byte is touched.  T == 0 returns RPA_OK.
+ * Bit-exact copy (FP8 caches: the codes defined at RPA_KV_FP8_E4M3); no other
+ * cache byte is touched.  T == 0 returns RPA_OK.
  */
 rpa_status rpa_write_kv(const rpa_shape *shape, const void *k_new, const void *v_new,
                         void *k_cache, void *v_cache, const int32_t *block_tables,
@@ -111,7 +127,7 @@ int32_t rpa_select_kernel(const rpa_shape *shape);
 /*
  * rpa_attention -- ragged paged causal GQA attention.
  *   q             device bf16 [T][Hq][D]
- *   k_cache, v_cache  device bf16 caches (layout per shape->layout)
+ *   k_cache, v_cache  device caches of shape->kv_dtype (layout per shape->layout)
  *   block_tables  device int32, see the layouts above; unused entries may be -1
  *   cu_q_lens     device int32 [B + 1], non-decreasing from 0 to T
  *   kv_lens       device int32 [B] (or [B][Hkv] for HEAD_MAJOR)
@@ -124,7 +140,8 @@ int32_t rpa_select_kernel(const rpa_shape *shape);
  *                 (may be NULL when that size is 0); its contents on entry do
  *                 not matter and are clobbered
  * For each row: out = softmax(scale * q K^T over keys 0 .. past + t) V, fp32
- * accumulate, rounded to bf16 (round to nearest even).  Sequences with
+ * accumulate, rounded to bf16 (round to nearest even); K and V are the cached
+ * values (FP8: code values times the scales).  Sequences with
  * q_len == 0 are skipped; T == 0 returns RPA_OK without a launch.
  */
 rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
@@ -162,6 +179,8 @@ typedef struct rpa_graph_shape {
   int32_t num_pages;
   int32_t max_pages_per_seq;
   int32_t layout;
+  int32_t kv_dtype;           /* as in rpa_shape */
+  float k_scale, v_scale;
 } rpa_graph_shape;
 
 /* Bytes of workspace rpa_graph_attention needs (plan, queue, split partials and

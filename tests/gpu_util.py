@@ -33,6 +33,20 @@ def to_host_f32(t):
     return t.float().cpu().numpy()
 
 
+def cache_dev(arr):
+    """A cache to the device: bf16 bit patterns, or FP8 codes (uint8) as they are."""
+    if arr.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+    return bf16_dev(arr)
+
+
+def cache_host(t):
+    """A device cache back as the oracle's array type (uint16 bf16 bits or uint8 codes)."""
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
+    return to_host_bits(t)
+
+
 class Dev:
     """Device copies of a RaggedBatch."""
 
@@ -41,8 +55,8 @@ class Dev:
         self.q = bf16_dev(b.q)
         self.k_new = bf16_dev(b.k_new)
         self.v_new = bf16_dev(b.v_new)
-        self.k_cache = bf16_dev(b.k_cache)
-        self.v_cache = bf16_dev(b.v_cache)
+        self.k_cache = cache_dev(b.k_cache)
+        self.v_cache = cache_dev(b.v_cache)
         self.tables = i32_dev(b.block_tables)
         self.cu = i32_dev(b.cu_q_lens)
         self.kvl = i32_dev(b.kv_lens)
@@ -58,20 +72,29 @@ class Dev:
                             v_new=self.v_new if fused_write else None,
                             cu_q_lens_host=self.cu_h,
                             kv_lens_host=self.kvl_h if kv_lens_host is None else kv_lens_host,
-                            kernel=kernel)
+                            kernel=kernel, k_scale=self.b.k_scale, v_scale=self.b.v_scale)
         torch.cuda.synchronize()
         return out
 
     def write(self):
         rpa.write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.tables, self.cu,
-                     self.kvl, cu_q_lens_host=self.cu_h, kv_lens_host=self.kvl_h)
+                     self.kvl, cu_q_lens_host=self.cu_h, kv_lens_host=self.kvl_h,
+                     k_scale=self.b.k_scale, v_scale=self.b.v_scale)
         torch.cuda.synchronize()
 
 
 def oracle_after_write(b: wl.RaggedBatch):
     """Caches after the oracle's scatter of the new tokens."""
     return oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new, b.k_cache,
-                           b.v_cache, b.page_size, layout=b.layout)
+                           b.v_cache, b.page_size, layout=b.layout, k_scale=b.k_scale,
+                           v_scale=b.v_scale)
+
+
+def oracle_attention(b: wl.RaggedBatch, k_cache, v_cache, **kw):
+    """The oracle's attention over the given caches (FP8 caches with the batch's scales)."""
+    return oracle.attention(b.q, k_cache, v_cache, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                            b.page_size, b.num_kv_heads, layout=b.layout, k_scale=b.k_scale,
+                            v_scale=b.v_scale, **kw)
 
 
 def sample_rows(b: wl.RaggedBatch, n, seed=0):

@@ -52,12 +52,13 @@ def test_library_has_no_oracle_dependency(lib):
     assert "oracle_" not in syms
 
 
-def _shape(cu, kv, Hq=4, Hkv=2, D=64, S=16, P=16, max_pages=4, layout=0, kernel=0):
+def _shape(cu, kv, Hq=4, Hkv=2, D=64, S=16, P=16, max_pages=4, layout=0, kernel=0, kv_dtype=0,
+           k_scale=1.0, v_scale=1.0):
     cu = np.ascontiguousarray(cu, np.int32)
     kv = np.ascontiguousarray(kv, np.int32)
     s = _rpa.RpaShape(len(cu) - 1, int(cu[-1]), Hq, Hkv, D, S, P, max_pages, layout, kernel,
                       cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                      kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+                      kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), kv_dtype, k_scale, v_scale)
     s._keep = (cu, kv)
     return s
 
@@ -78,6 +79,9 @@ def _attn(lib, s, scale=0.125, k_new=None, ws=None, ws_bytes=0, ptr=16):
     (dict(cu=[0, 1], kv=[4], S=8), "power of two"),
     (dict(cu=[0, 1], kv=[4], layout=5), "layout"),
     (dict(cu=[0, 1], kv=[4], kernel=9), "kernel"),
+    (dict(cu=[0, 1], kv=[4], kv_dtype=3), "kv_dtype"),
+    (dict(cu=[0, 1], kv=[4], kv_dtype=1, k_scale=-1.0), "scale"),
+    (dict(cu=[0, 1], kv=[4], kv_dtype=1, v_scale=float("nan")), "scale"),
 ])
 def test_invalid_arguments(lib, kw, frag):
     s = _shape(**kw)
@@ -102,6 +106,12 @@ def test_bad_scale_and_pointer_checks(lib):
     assert lib.rpa_attention(ctypes.byref(s), p, p, p, p, p, p, 0.125, p, None, p, None, 0,
                              None) == 1
     assert "both" in lib.rpa_last_error().decode()
+
+
+def test_bf16_cache_ignores_scales(lib):
+    """The scales are read only for FP8 caches."""
+    s = _shape([0, 0, 0], [5, 9], k_scale=0.0, v_scale=float("nan"))
+    assert _attn(lib, s, ptr=0) == 0
 
 
 def test_empty_batch_is_ok_without_device(lib):
@@ -162,7 +172,8 @@ def test_union_builder_validation(lib):
 
 def _gshape(**kw):
     f = dict(max_seqs=4, max_tokens=32, max_splits=8, num_q_heads=8, num_kv_heads=2, head_dim=128,
-             page_size=16, num_pages=64, max_pages_per_seq=16, layout=0)
+             page_size=16, num_pages=64, max_pages_per_seq=16, layout=0, kv_dtype=0, k_scale=1.0,
+             v_scale=1.0)
     f.update(kw)
     return _rpa.RpaGraphShape(*[f[n] for n, _ in _rpa.RpaGraphShape._fields_])
 
@@ -176,6 +187,10 @@ def _gshape(**kw):
     (dict(page_size=24), "page_size"),
     (dict(page_size=2048), "page_size"),
     (dict(layout=3), "layout"),
+    (dict(kv_dtype=2), "kv_dtype"),
+    (dict(kv_dtype=1, k_scale=0.0), "scale"),
+    (dict(kv_dtype=1, v_scale=float("inf")), "scale"),
+    (dict(kv_dtype=1, k_scale=1e-39), "scale"),
 ])
 def test_graph_shape_validation(lib, kw, frag):
     s = _gshape(**kw)
