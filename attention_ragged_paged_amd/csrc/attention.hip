@@ -184,7 +184,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   // FP8 cache: a lane loads 16 codes (16 bytes) of a row; new keys come as 32 bytes of bf16.
   constexpr int LPR8 = D / 16;     // lanes per row
   constexpr int RPI8 = 64 / LPR8;  // rows per load instruction
-  constexpr int NI8 = 16 / RPI8;   // load instructions per 16-key chunk (registers: 2 per)
+  constexpr int NI8 = 16 / RPI8;   // load instructions per 16-key chunk
   DecodeSmem<D> &sm = *reinterpret_cast<DecodeSmem<D> *>(smem_raw);
   const int tid = item_tid();
   const int lane = tid & 63;
@@ -248,27 +248,30 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   // instruction t brings rows lrow + RPI*t.  Rows of new keys come from k_new / v_new.
   const uint8_t *const k8 = reinterpret_cast<const uint8_t *>(a.k_cache);
   const uint8_t *const v8 = reinterpret_cast<const uint8_t *>(a.v_cache);
+  // FP8: element offset of this lane's 16 values of new key `key` in k_new / v_new (keys past
+  // the sequence's end, in a chunk's tail, read its last new row instead)
+  auto new_off = [&](int key) {
+    return ((int64_t)(q0 + min(key, kv_len - 1) - past) * a.Hkv + g) * D + 16 * lchk;
+  };
   auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
     const int page = __builtin_amdgcn_readlane(pg_lane, i);
     if constexpr (KV8) {
-      // registers 2t, 2t+1: the row's codes (cached key) or its 16 bf16 values (new key)
+      // register t: the row's 16 codes, or for a new key the first 8 of its bf16 values (the
+      // other 8 are loaded when the chunk is staged); every lane loads, so the waits before
+      // each chunk's use stay exact
 #pragma unroll
       for (int t = 0; t < NI8; ++t) {
         const int r = lrow + RPI8 * t;
         const int key = key0 + r;
+        const uint8_t *kp = k8 + kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
+        const uint8_t *vp = v8 + (kp - k8);
         if (fused && key >= past) {
-          // keys past the sequence's end (the chunk's tail) read its last new row instead
-          const int64_t noff = ((int64_t)(q0 + min(key, kv_len - 1) - past) * a.Hkv + g) * D + 16 * lchk;
-          kr[2 * t] = *reinterpret_cast<const u32x4 *>(a.k_new + noff);
-          kr[2 * t + 1] = *reinterpret_cast<const u32x4 *>(a.k_new + noff + 8);
-          vr[2 * t] = *reinterpret_cast<const u32x4 *>(a.v_new + noff);
-          vr[2 * t + 1] = *reinterpret_cast<const u32x4 *>(a.v_new + noff + 8);
-        } else {
-          const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
-          kr[2 * t] = *reinterpret_cast<const u32x4 *>(k8 + coff);
-          vr[2 * t] = *reinterpret_cast<const u32x4 *>(v8 + coff);
+          kp = reinterpret_cast<const uint8_t *>(a.k_new + new_off(key));
+          vp = reinterpret_cast<const uint8_t *>(a.v_new + new_off(key));
         }
+        kr[t] = *reinterpret_cast<const u32x4 *>(kp);
+        vr[t] = *reinterpret_cast<const u32x4 *>(vp);
       }
       return;
     }
@@ -301,10 +304,12 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
       for (int t = 0; t < NI8; ++t) {
         const int r = lrow + RPI8 * t;
         const int key = key0 + r;
-        u32x4 kc = kr[2 * t], vc = vr[2 * t];
+        u32x4 kc = kr[t], vc = vr[t];
         if (fused && key >= past) {
-          kc = quantize16(kr[2 * t], kr[2 * t + 1], a.k_inv);
-          vc = quantize16(vr[2 * t], vr[2 * t + 1], a.v_inv);
+          const u32x4 khi = *reinterpret_cast<const u32x4 *>(a.k_new + new_off(key) + 8);
+          const u32x4 vhi = *reinterpret_cast<const u32x4 *>(a.v_new + new_off(key) + 8);
+          kc = quantize16(kr[t], khi, a.k_inv);
+          vc = quantize16(vr[t], vhi, a.v_inv);
           if (writer && key < k_end) {
             const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
             *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(k8) + coff) = kc;
@@ -379,6 +384,33 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   for (int base = 0; base < n_w; base += 64) {
     const int n = min(64, n_w - base);
     pg_lane = lane < n ? table_at(a, b, g, (k_begin + 16 * (w + 4 * (base + lane))) >> a.page_shift) : 0;
+    if constexpr (KV8) {
+      // An FP8 chunk is half the bytes of a bf16 one: four chunks stay in flight (a register
+      // ring) so that a wave keeps as many bytes in flight as the bf16 loop does.
+      u32x4 k0[NI8], v0[NI8], k1[NI8], v1[NI8], k2[NI8], v2[NI8], k3[NI8], v3[NI8];
+      load_chunk(base, 0, k0, v0);
+      load_chunk(base, min(1, n - 1), k1, v1);
+      load_chunk(base, min(2, n - 1), k2, v2);
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        load_chunk(base, min(i + 3, n - 1), k3, v3);
+        __builtin_amdgcn_sched_barrier(0);
+        process_chunk(base, i, k0, v0);
+        load_chunk(base, min(i + 4, n - 1), k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        process_chunk(base, i + 1, k1, v1);
+        load_chunk(base, min(i + 5, n - 1), k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        process_chunk(base, i + 2, k2, v2);
+        load_chunk(base, min(i + 6, n - 1), k2, v2);
+        __builtin_amdgcn_sched_barrier(0);
+        process_chunk(base, i + 3, k3, v3);
+      }
+      if (i < n) process_chunk(base, i, k0, v0);
+      if (i + 1 < n) process_chunk(base, i + 1, k1, v1);
+      if (i + 2 < n) process_chunk(base, i + 2, k2, v2);
+      continue;
+    }
     u32x4 kA[KK], vA[KK], kB[KK], vB[KK];
     load_chunk(base, 0, kA, vA);
     // Two chunks per trip, register double buffer.  Every load is unconditional (the last

@@ -17,6 +17,9 @@ Workloads (all seeded synthetic inputs with Llama-3-8B attention shapes, 32/8 he
   mixed_chunked       one 512-token chunk at context 8192 + 96 decodes, page 16
   block_union_sparse  4096-query chunk at context 131072, KV-head-major page 64, 10% block mask
   tiny_ragged         the 3-sequence parity case (latency only)
+  llama3_decode_fp8, mixed_chunked_fp8
+                      the same batches over FP8 E4M3 K/V caches (1 byte an element, per-cache
+                      scales; new K/V quantized by the call)
 
 `value` is the step's algorithmic throughput: GB/s for the HBM-bound decode and mixed
 batches, TFLOP/s for the MFMA-bound prefill and sparse ones.  `roofline` rates the
@@ -42,7 +45,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode HBM GB/s (% peak) + prefill/mixed TFLOP/s (% MFMA peak), tokens/s"
 WORKLOAD_BOUND = {"llama3_decode": "hbm", "mixed_chunked": "hbm", "tiny_ragged": "hbm",
-                  "llama3_prefill": "mfma", "block_union_sparse": "mfma"}
+                  "llama3_prefill": "mfma", "block_union_sparse": "mfma",
+                  "llama3_decode_fp8": "hbm", "mixed_chunked_fp8": "hbm"}
 
 
 def log(msg):
@@ -55,18 +59,19 @@ def step_bytes(b, attention_only=False):
     """Algorithmic HBM bytes: every K/V byte of every visible key read once per KV head, Q read,
     O written, block tables and lengths read; plus (whole step) new K/V read and written."""
     D, Hkv, Hq = b.head_dim, b.num_kv_heads, b.num_q_heads
+    eb = 1 if b.kv_fp8 else 2   # bytes per cached element
     kv = b.kv_lens.reshape(b.num_seqs, -1)
     if b.layout == 0:
-        kv_bytes = int(kv[:, 0].astype(np.int64).sum()) * Hkv * D * 2 * 2
+        kv_bytes = int(kv[:, 0].astype(np.int64).sum()) * Hkv * D * eb * 2
         tables = int(((kv[:, 0] + b.page_size - 1) // b.page_size).sum()) * 4
     else:
-        kv_bytes = int(kv.astype(np.int64).sum()) * D * 2 * 2
+        kv_bytes = int(kv.astype(np.int64).sum()) * D * eb * 2
         tables = int(((kv + b.page_size - 1) // b.page_size).sum()) * 4
     qo = b.total_q * Hq * D * 2 * 2
     meta = (b.num_seqs + 1) * 4 + kv.size * 4
     total = kv_bytes + qo + tables + meta
     if not attention_only:
-        total += b.total_q * Hkv * D * 2 * 2 * 2
+        total += b.total_q * Hkv * D * (2 + eb) * 2   # new K/V: bf16 read, cache element written
     return total
 
 
@@ -114,7 +119,8 @@ def cpu_baseline(b, workload, bound, budget_s=12.0):
     """The oracle (unmodified) on the host cores over a bounded sample of the same batch."""
     import oracle
     kc, vc = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
-                             b.k_cache, b.v_cache, b.page_size, layout=b.layout)
+                             b.k_cache, b.v_cache, b.page_size, layout=b.layout,
+                             k_scale=b.k_scale, v_scale=b.v_scale)
     threads = oracle.num_threads()
     rows_all = b.total_q * b.num_q_heads
     block_allowed = b.extra.get("allowed")
@@ -130,7 +136,7 @@ def cpu_baseline(b, workload, bound, budget_s=12.0):
         oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
                          b.page_size, b.num_kv_heads, layout=b.layout,
                          block_allowed=block_allowed, rows=None if stride == 1 else rows,
-                         nthreads=threads)
+                         nthreads=threads, k_scale=b.k_scale, v_scale=b.v_scale)
         reps += 1
         if time.perf_counter() - t0 >= 0.8 * budget_s or reps >= 1000:
             break
@@ -197,8 +203,12 @@ def main():
     def to_dev_i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
 
+    def to_dev_cache(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev) if a.dtype == np.uint8 \
+            else to_dev_bf16(a)
+
     q, kn, vn = to_dev_bf16(b.q), to_dev_bf16(b.k_new), to_dev_bf16(b.v_new)
-    kc, vc = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    kc, vc = to_dev_cache(b.k_cache), to_dev_cache(b.v_cache)
     base_tables = to_dev_i32(b.block_tables)
     cu, kvl = to_dev_i32(b.cu_q_lens), to_dev_i32(b.kv_lens)
     cu_h = torch.from_numpy(np.ascontiguousarray(b.cu_q_lens, np.int32))
@@ -232,10 +242,11 @@ def main():
     # the compacted union tables, whose last blocks are the chunk's own pages (same page and
     # slot for every new key as the base tables give).
     attn = rpa.PreparedAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, k_new=kn, v_new=vn,
-                                 cu_q_lens_host=cu_h, kv_lens_host=att_kvl_h)
+                                 cu_q_lens_host=cu_h, kv_lens_host=att_kvl_h, k_scale=b.k_scale,
+                                 v_scale=b.v_scale)
     if args.path == "graph":
         ga = rpa.GraphAttention(q, kc, vc, att_tables, cu, att_kvl, b.scale, k_new=kn, v_new=vn,
-                                max_splits=16)
+                                max_splits=16, k_scale=b.k_scale, v_scale=b.v_scale)
         ga()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -243,7 +254,8 @@ def main():
             ga()
         torch.cuda.synchronize()
         attn = graph.replay
-    kind = rpa.select_kernel(q, kc, att_tables, cu_h, att_kvl_h)
+    kind = rpa.select_kernel(q, kc, att_tables, cu_h, att_kvl_h, k_scale=b.k_scale,
+                             v_scale=b.v_scale)
     flush_buf = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def flush():
@@ -322,8 +334,11 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 values, Llama-3-8B attention shapes)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (q, out, new K/V), fp8-e4m3 K/V cache" if b.kv_fp8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) bf16 values, FP8 cache codes drawn per field, "
+                 "Llama-3-8B attention shapes)" if b.kv_fp8 else
+                 "synthetic (seeded N(0,1) bf16 values, Llama-3-8B attention shapes)"),
         "config": cfg,
         "tokens_per_s": round(b.total_q / (ms * 1e-3), 1),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 5) for p in (10, 50, 90)],

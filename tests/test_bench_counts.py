@@ -25,17 +25,19 @@ def _brute_flops(b):
 
 def _brute_bytes(b):
     D, Hq, Hkv, S = b.head_dim, b.num_q_heads, b.num_kv_heads, b.page_size
+    eb = b.k_cache.itemsize                             # bytes per cached element
     kv = b.kv_lens.reshape(b.num_seqs, -1)
     total = 0
     for s in range(b.num_seqs):
         for g in range(Hkv):
             L = int(kv[s, g if kv.shape[1] > 1 else 0])
-            total += L * D * 2 * 2                      # K and V rows of this KV head
+            total += L * D * eb * 2                     # K and V rows of this KV head
             if kv.shape[1] > 1 or g == 0:               # one table per sequence (per head if head-major)
                 total += -(-L // S) * 4
     total += b.total_q * Hq * D * 2 * 2                 # Q read, O written
     total += (b.num_seqs + 1) * 4 + kv.size * 4         # cu_q_lens, kv_lens
-    total += b.total_q * Hkv * D * 2 * 2 * 2            # new K/V read and written
+    total += b.total_q * Hkv * D * 2 * 2                # new K/V read (bf16)
+    total += b.total_q * Hkv * D * eb * 2               # and written into the caches
     return total
 
 
@@ -44,6 +46,8 @@ def _brute_bytes(b):
     lambda: wl.ragged_batch("c", [3, 1, 0, 17], [40, 9, 5, 17], 8, 2, 64, 16, 20, 7),
     lambda: wl.ragged_batch("h", [5, 1], np.array([[30, 12], [9, 44]]), 8, 2, 128, 16, 20, 8,
                             layout=wl.HEAD_MAJOR),
+    lambda: wl.ragged_batch("f", [3, 1, 0, 17], [40, 9, 5, 17], 8, 2, 64, 16, 20, 7,
+                            kv_dtype="fp8"),
 ])
 def test_counts_match_brute_force(make):
     b = make()
