@@ -355,11 +355,18 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
       sv[i4] = ok ? st[i4] * a.scale_log2 : kNegInf;
       mloc = fmaxf(mloc, sv[i4]);
     }
-    mloc = wave_max_xor(mloc, 16);
-    mloc = wave_max_xor(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    mloc = pair_max32(pair_max16(mloc));  // the row's 4 lanes: l, l ^ 16, l ^ 32, l ^ 48
+    // Lazy rescale: the running max moves only when a row's max grows by more than 8 (log2
+    // units), so probabilities stay below 2^8 and most chunks skip rescaling the accumulators.
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = acc[mb] * alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float p[4];
     float psum = 0.f;
 #pragma unroll
@@ -367,8 +374,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
       p[i4] = fast_exp2(sv[i4] - m_use);
       psum += p[i4];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
     const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
     // Transposing read: lane (i = l%16, j) names row 4j + i/4, dims 16mb + 4(i%4) .. +3.
     const int tr_row = 4 * j + (r16 >> 2);
@@ -376,7 +382,6 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
     for (int mb = 0; mb < MB; ++mb) {
       const int c = 2 * mb + ((r16 & 3) >> 1);
       const s16x4 va = lds_read_tr(vbuf + lds_off<D>(tr_row, c) + 4 * (r16 & 1));
-      acc[mb] = acc[mb] * alpha;
       acc[mb] = mfma16x16x16(va, pb, acc[mb]);
     }
   };
