@@ -12,6 +12,7 @@ Functions (each cites the passage it follows in ``rpa_oracle.c``):
   write_kv        scatter of new K/V rows into their page slots
   attention       page gather + softmax attention, fp64, all rows or sampled rows
   union_tables    Q-block union -> intra-group union -> ascending compaction
+  rotary_qkv      rotary embedding of new Q/K (packed or separate Q, K, V), then the scatter
   fp8_encode, fp8_decode
                   FP8 E4M3 (OCP) codes of a quantized cache; write_kv and attention
                   take uint8 caches with per-tensor k_scale / v_scale as FP8 caches
@@ -70,6 +71,10 @@ def _load():
         lib.oracle_fp8_encode.restype = i
         lib.oracle_fp8_decode.argtypes = [p, p, ctypes.c_int64]
         lib.oracle_fp8_decode.restype = i
+        lib.oracle_rotary_qkv.argtypes = [i, p, p, i, i, i, i, i, i, i, p, p, p, p,
+                                          ctypes.c_int64, ctypes.c_int64, p, p, i, i, i, p, p, p,
+                                          i, ctypes.c_float, ctypes.c_float]
+        lib.oracle_rotary_qkv.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -133,6 +138,39 @@ def write_kv(cu_q_lens, kv_lens, tables, k_new, v_new, k_cache, v_cache, page_si
     if rc != 0:
         raise ValueError(f"oracle_write_kv failed with code {rc}")
     return kc, vc
+
+
+def rotary_qkv(cu_q_lens, kv_lens, tables, q, k, v, k_cache, v_cache, page_size, cos_cache,
+               sin_cache, rotary_dim, interleaved, layout=SEQ_MAJOR, k_scale=1.0, v_scale=1.0):
+    """Rotary embedding of the new rows, then their scatter.
+
+    q [T, Hq, D], k and v [T, Hkv, D] (uint16 bf16 bits; a packed [T, Hq + 2 Hkv, D] array is
+    split by slicing); cos_cache, sin_cache float32 [max_position, rotary_dim / 2].
+    Returns (q_out [T, Hq, D], k_cache', v_cache') with the caches copied, not modified.
+    uint8 caches are FP8 caches with scales k_scale, v_scale."""
+    lib = _load()
+    cu = _c(cu_q_lens, np.int32)
+    kl = _c(kv_lens, np.int32)
+    tb = _c(tables, np.int32)
+    qq, kk, vv = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    T, Hq, D = qq.shape
+    Hkv = kk.shape[1]
+    kv8 = np.asarray(k_cache).dtype == np.uint8
+    cdt = np.uint8 if kv8 else np.uint16
+    kc = np.array(k_cache, dtype=cdt, copy=True, order="C")
+    vc = np.array(v_cache, dtype=cdt, copy=True, order="C")
+    cs = _c(cos_cache, np.float32)
+    sn = _c(sin_cache, np.float32)
+    q_out = np.zeros((T, Hq, D), dtype=np.uint16)
+    B = cu.shape[0] - 1
+    rc = lib.oracle_rotary_qkv(B, _ptr(cu), _ptr(kl), Hq, Hkv, D, int(page_size), layout,
+                               tb.shape[-1], kc.shape[0], _ptr(tb), _ptr(qq), _ptr(kk), _ptr(vv),
+                               Hq * D, Hkv * D, _ptr(cs), _ptr(sn), cs.shape[0] if cs.ndim else 0,
+                               int(rotary_dim), int(bool(interleaved)), _ptr(q_out), _ptr(kc),
+                               _ptr(vc), int(kv8), float(k_scale), float(v_scale))
+    if rc != 0:
+        raise ValueError(f"oracle_rotary_qkv failed with code {rc}")
+    return q_out, kc, vc
 
 
 def attention(q, k_cache, v_cache, tables, cu_q_lens, kv_lens, scale, page_size,

@@ -21,6 +21,18 @@
  *   oracle_union_tables   Q-block union, then intra-group union, then ascending
  *                         compaction into per-KV-head tables (CompactAttention page,
  *                         "Core claim" and Figure 3; KV-head-major pages, Figure 4).
+ *   oracle_rotary_qkv     rotary embedding of new Q and K rows taken from packed or
+ *                         separate Q/K/V, then the K/V scatter (ONNX Runtime PR, the rotary
+ *                         program of Phase 1b.2: rotate Q and K before the scatter,
+ *                         position = past + local token, dims from rotary_dim on copied,
+ *                         V not rotated, interleaved or split pairs; and the packed-QKV
+ *                         commit: per token, columns [0, Hq*D) are Q, then Hkv*D of K, then
+ *                         Hkv*D of V).  Pair (x1, x2) at position p and pair index i becomes
+ *                         (x1 cos - x2 sin, x2 cos + x1 sin) with cos = cos_cache[p][i],
+ *                         sin = sin_cache[p][i] (fp32 tables [max_position][rotary_dim/2]);
+ *                         interleaved pairs are dims (2i, 2i+1), split pairs (i, i + rd/2).
+ *                         Each output is fmaf(x1, cos, -(x2 * sin)), resp.
+ *                         fmaf(x2, cos, x1 * sin), in fp32, rounded to bf16 (nearest even).
  *   oracle_fp8_encode, oracle_fp8_decode, oracle_write_kv_fp8, oracle_attention_fp8
  *                         the quantized KV cache that the ONNX Runtime PR lists among
  *                         its deferred items ("Quantized KV cache (T_CACHE)") without
@@ -434,4 +446,105 @@ int oracle_union_tables(const uint8_t *mask, int Hq, int Hkv, int nQB, int nKB,
     }
     free(sel);
     return 0;
+}
+
+/* fp32 -> bf16 bits, round to nearest even (finite values). */
+static uint16_t float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* One row of D values (bf16 bits) rotated at position pos; dims >= rd are copied. */
+static void rotate_row(const uint16_t *x, uint16_t *y, int D, int rd, int interleaved,
+                       const float *cos_row, const float *sin_row)
+{
+    for (int d = 0; d < D; ++d) {
+        if (d >= rd) {
+            y[d] = x[d];
+            continue;
+        }
+        int half = rd / 2;
+        int i, first, partner;
+        if (interleaved) {
+            i = d / 2;
+            first = (d % 2) == 0;
+            partner = first ? d + 1 : d - 1;
+        } else {
+            i = d < half ? d : d - half;
+            first = d < half;
+            partner = first ? d + half : d - half;
+        }
+        float c = cos_row[i], s = sin_row[i];
+        float xd = (float)bf16_to_double(x[d]);
+        float xp = (float)bf16_to_double(x[partner]);
+        float out = first ? fmaf(xd, c, -(xp * s)) : fmaf(xd, c, xp * s);
+        y[d] = float_to_bf16(out);
+    }
+}
+
+/*
+ * q, k, v: the new rows; row t of head h at q + t * q_stride + h * D (likewise k, v with
+ * kv_stride); packed QKV is q = qkv, k = qkv + Hq*D, v = qkv + (Hq+Hkv)*D with both strides
+ * (Hq + 2 Hkv) * D.  Writes q_out [T][Hq][D] (rotated) and scatters rotated K and V into the
+ * caches exactly as oracle_write_kv / oracle_write_kv_fp8 do (kv8, scales).  rd == 0 rotates
+ * nothing.  The position of token t of sequence b is kv_len(b, KV head 0) - q_len_b + t.
+ * Returns 1 on a bad argument (odd or too large rd, a position >= max_position).
+ */
+int oracle_rotary_qkv(int B, const int32_t *cu_q_lens, const int32_t *kv_lens,
+                      int Hq, int Hkv, int D, int S, int layout, int max_pages, int num_pages,
+                      const int32_t *tables, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, int64_t q_stride, int64_t kv_stride,
+                      const float *cos_cache, const float *sin_cache, int max_position,
+                      int rd, int interleaved, uint16_t *q_out, void *k_cache, void *v_cache,
+                      int kv8, float k_scale, float v_scale)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || rd < 0 || rd > D || rd % 2 != 0)
+        return 1;
+    int64_t T = cu_q_lens[B];
+    uint16_t *kn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * Hkv * D + 1));
+    uint16_t *vn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * Hkv * D + 1));
+    if (!kn || !vn) {
+        free(kn);
+        free(vn);
+        return 1;
+    }
+    int rc = 0;
+    for (int b = 0; b < B && rc == 0; ++b) {
+        int q_len = cu_q_lens[b + 1] - cu_q_lens[b];
+        int past = kv_len_of(kv_lens, layout, Hkv, b, 0) - q_len;
+        for (int t = 0; t < q_len && rc == 0; ++t) {
+            int64_t tok = cu_q_lens[b] + t;
+            int pos = past + t;
+            if (rd > 0 && (pos < 0 || pos >= max_position)) {
+                rc = 1;
+                break;
+            }
+            const float *cr = rd > 0 ? cos_cache + (int64_t)pos * (rd / 2) : NULL;
+            const float *sr = rd > 0 ? sin_cache + (int64_t)pos * (rd / 2) : NULL;
+            for (int h = 0; h < Hq; ++h)
+                rotate_row(q + tok * q_stride + (int64_t)h * D, q_out + (tok * Hq + h) * D, D,
+                           rd, interleaved, cr, sr);
+            for (int g = 0; g < Hkv; ++g) {
+                rotate_row(k + tok * kv_stride + (int64_t)g * D, kn + (tok * Hkv + g) * D, D, rd,
+                           interleaved, cr, sr);
+                memcpy(vn + (tok * Hkv + g) * D, v + tok * kv_stride + (int64_t)g * D,
+                       sizeof(uint16_t) * (size_t)D);
+            }
+        }
+    }
+    if (rc == 0) {
+        if (kv8)
+            rc = oracle_write_kv_fp8(B, cu_q_lens, kv_lens, Hkv, D, S, layout, max_pages,
+                                     num_pages, tables, kn, vn, (uint8_t *)k_cache,
+                                     (uint8_t *)v_cache, k_scale, v_scale);
+        else
+            rc = oracle_write_kv(B, cu_q_lens, kv_lens, Hkv, D, S, layout, max_pages, num_pages,
+                                 tables, kn, vn, (uint16_t *)k_cache, (uint16_t *)v_cache);
+    }
+    free(kn);
+    free(vn);
+    return rc;
 }

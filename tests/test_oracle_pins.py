@@ -490,3 +490,94 @@ def test_fp8_attention_scales_are_linear():
                             v_scale=1.0)
     got = oracle.attention(*args, b.scale, b.page_size, b.num_kv_heads, k_scale=0.37, v_scale=1.7)
     np.testing.assert_allclose(got, 1.7 * base, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------- rotary embedding and packed QKV ----
+# The ONNX Runtime PR's rotary program rotates Q and K before the scatter (position = past +
+# local token, dims from rotary_dim on copied, V untouched) with interleaved or split pairs.
+
+def _rope_tables(max_pos, rd, seed):
+    rng = np.random.default_rng(seed)
+    theta = rng.uniform(-np.pi, np.pi, size=(max_pos, rd // 2))   # every (position, pair) distinct
+    return np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+
+
+def _rope_batch(layout=wl.SEQ_MAJOR, kv_dtype="bf16"):
+    return wl.ragged_batch("rope", [3, 1, 6], [3, 20, 38], 8, 2, 64, 16, 12, 17, layout=layout,
+                           kv_dtype=kv_dtype)
+
+
+def test_rotary_identity_tables_give_the_plain_scatter():
+    """cos = 1, sin = 0 (or rotary_dim 0): Q unchanged, caches equal the pinned scatter.
+    Catches: a rotation applied where none is asked for, V rotated, a wrong slot."""
+    b = _rope_batch()
+    ones, zeros = np.ones((64, 32), np.float32), np.zeros((64, 32), np.float32)
+    k2, v2 = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                             b.k_cache, b.v_cache, b.page_size)
+    for rd, inter in [(64, False), (64, True), (0, False)]:
+        qo, kc, vc = oracle.rotary_qkv(b.cu_q_lens, b.kv_lens, b.block_tables, b.q, b.k_new,
+                                       b.v_new, b.k_cache, b.v_cache, b.page_size, ones, zeros,
+                                       rd, inter)
+        assert np.array_equal(qo, b.q) and np.array_equal(kc, k2) and np.array_equal(vc, v2)
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("rd", [64, 32, 16])
+def test_rotary_is_complex_multiplication_at_past_plus_t(interleaved, rd):
+    """Each pair, read as the complex number x1 + i x2, is multiplied by cos + i sin of its
+    position past + t (numpy complex128), then rounded to bf16; dims from rd on and all of V
+    are copied bit for bit.  Catches: a wrong pair layout, a sign, the position off by one,
+    the tables indexed by the wrong pair."""
+    b = _rope_batch()
+    cos, sin = _rope_tables(64, rd, 4)
+    qo, kc, vc = oracle.rotary_qkv(b.cu_q_lens, b.kv_lens, b.block_tables, b.q, b.k_new, b.v_new,
+                                   b.k_cache, b.v_cache, b.page_size, cos, sin, rd, interleaved)
+    pos = np.concatenate([np.arange(q) + (kv - q) for q, kv in zip(np.diff(b.cu_q_lens), b.kv_lens)])
+
+    def ref(x):   # x: bf16 bits [T, H, D]
+        f = wl.bf16_to_f32(x).astype(np.float64)
+        if interleaved:
+            z = f[..., 0:rd:2] + 1j * f[..., 1:rd:2]
+        else:
+            z = f[..., :rd // 2] + 1j * f[..., rd // 2:rd]
+        rot = z * (cos[pos] + 1j * sin[pos])[:, None, :]
+        out = f.copy()
+        if interleaved:
+            out[..., 0:rd:2], out[..., 1:rd:2] = rot.real, rot.imag
+        else:
+            out[..., :rd // 2], out[..., rd // 2:rd] = rot.real, rot.imag
+        return out
+
+    got_q = wl.bf16_to_f32(qo).astype(np.float64)
+    want_q = ref(b.q)
+    np.testing.assert_allclose(got_q, want_q, rtol=2 ** -8, atol=1e-6)
+    assert np.array_equal(qo[..., rd:], b.q[..., rd:])
+    # K was rotated the same way before the scatter; V not at all
+    kr = wl.bf16_bits(ref(b.k_new).astype(np.float32))
+    k_plain, v_plain = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, kr, b.v_new,
+                                       b.k_cache, b.v_cache, b.page_size)
+    diff = wl.bf16_to_f32(kc).astype(np.float64) - wl.bf16_to_f32(k_plain).astype(np.float64)
+    assert np.abs(diff).max() <= 2 ** -7 * np.abs(wl.bf16_to_f32(k_plain)).max()
+    assert np.array_equal(vc, v_plain)
+
+
+def test_rotary_fp8_cache_stores_the_rotated_keys_codes():
+    """Over an FP8 cache the scatter stores the codes of the rotated bf16 keys: the same as
+    the pinned FP8 scatter fed with the oracle's own rotated keys."""
+    b = _rope_batch(kv_dtype="fp8")
+    cos, sin = _rope_tables(64, 64, 5)
+    qo, kc, vc = oracle.rotary_qkv(b.cu_q_lens, b.kv_lens, b.block_tables, b.q, b.k_new, b.v_new,
+                                   b.k_cache, b.v_cache, b.page_size, cos, sin, 64, False,
+                                   k_scale=b.k_scale, v_scale=b.v_scale)
+    # the rotated bf16 keys, recovered from a bf16 run of the same rotation
+    zeros16 = np.zeros(b.k_cache.shape, np.uint16)
+    _, k16, _ = oracle.rotary_qkv(b.cu_q_lens, b.kv_lens, b.block_tables, b.q, b.k_new, b.v_new,
+                                  zeros16, zeros16, b.page_size, cos, sin, 64, False)
+    ones = np.ones_like(b.k_new)
+    wmask, _ = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, ones, ones, zeros16,
+                               zeros16, b.page_size)
+    written = wmask != 0
+    x = (wl.bf16_to_f32(k16[written]) * (np.float32(1) / np.float32(b.k_scale))).astype(np.float32)
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(kc[written], want)
+    assert np.array_equal(kc[~written], b.k_cache[~written])
