@@ -7,6 +7,7 @@ CPU fallback: every call fails loudly if the library or a gfx950 device is missi
     write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, ...)
     attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, ...)
     build_union_tables(mask, base_tables, past, kv_len, page_size)
+    rotary_write_kv(q, k, v, k_cache, v_cache, ...)   # rotary + packed-QKV split + scatter
     GraphAttention(...)   # device-planned call that a HIP graph can capture
 
 Caches are bf16, or FP8 E4M3 codes (uint8 / float8_e4m3fn storage) with per-cache scales
@@ -30,7 +31,9 @@ from ._rpa import (  # noqa: F401
     kv_dtype_of,
     library_path,
     load_library,
+    rotary_write_kv,
     select_kernel,
+    split_packed_qkv,
     workspace_size,
     write_kv,
 )

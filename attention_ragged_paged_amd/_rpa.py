@@ -28,7 +28,7 @@ _STATUS = {0: "RPA_OK", 1: "RPA_ERR_INVALID_ARGUMENT", 2: "RPA_ERR_UNSUPPORTED",
 
 EXPORTED = ("rpa_write_kv", "rpa_attention_workspace_size", "rpa_select_kernel", "rpa_attention",
             "rpa_graph_workspace_size", "rpa_graph_attention", "rpa_build_union_tables",
-            "rpa_last_error")
+            "rpa_rotary_write_kv", "rpa_last_error")
 
 
 class RpaError(RuntimeError):
@@ -83,6 +83,9 @@ def load_library():
     shp = ctypes.POINTER(RpaShape)
     lib.rpa_write_kv.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.rpa_write_kv.restype = ctypes.c_int
+    lib.rpa_rotary_write_kv.argtypes = [shp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.POINTER(RpaRotary), vp, vp, vp, vp, vp, vp, vp]
+    lib.rpa_rotary_write_kv.restype = ctypes.c_int
     lib.rpa_attention_workspace_size.argtypes = [shp]
     lib.rpa_attention_workspace_size.restype = sz
     lib.rpa_select_kernel.argtypes = [shp]
@@ -142,6 +145,12 @@ def kv_dtype_of(k_cache, v_cache=None):
     return d
 
 
+class RpaRotary(ctypes.Structure):
+    _fields_ = [("cos_cache", ctypes.c_void_p), ("sin_cache", ctypes.c_void_p),
+                ("max_position", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+                ("interleaved", ctypes.c_int32)]
+
+
 class _Shape:
     """An RpaShape plus the host tensors it points into (kept alive with it)."""
 
@@ -193,6 +202,53 @@ def write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *
     _check(lib.rpa_write_kv(shape.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                             _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens),
                             _stream(k_cache.device)))
+
+
+def _row_view(t, heads, name):
+    """(pointer, row stride in elements) of a [T, heads, D] view whose rows may be strided
+    (a slice of packed QKV); dims and heads must be dense within a row."""
+    if t.dim() != 3 or t.shape[1] != heads or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [T, {heads}, D] with dense heads and dims")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0)
+
+
+def split_packed_qkv(qkv, num_q_heads, num_kv_heads):
+    """Views q [T, Hq, D], k and v [T, Hkv, D] of packed QKV [T, (Hq + 2 Hkv) * D] (no copy)."""
+    T = qkv.shape[0]
+    x = qkv.reshape(T, num_q_heads + 2 * num_kv_heads, -1)
+    return (x[:, :num_q_heads], x[:, num_q_heads:num_q_heads + num_kv_heads],
+            x[:, num_q_heads + num_kv_heads:])
+
+
+def rotary_write_kv(q, k, v, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, *,
+                    cos_cache=None, sin_cache=None, rotary_dim=0, interleaved=False, q_out=None,
+                    cu_q_lens_host=None, kv_lens_host=None, k_scale=1.0, v_scale=1.0):
+    """Rotate the new rows of Q and K, write the rotated Q to q_out and scatter K and V into
+    the caches (rpa_rotary_write_kv).  q [T, Hq, D], k and v [T, Hkv, D] bf16, which may be
+    strided row views of packed QKV (see split_packed_qkv); cos_cache, sin_cache fp32
+    [max_position, rotary_dim / 2].  Returns q_out."""
+    lib = load_library()
+    Hq, Hkv = q.shape[1], k.shape[1]
+    qp, qs = _row_view(q, Hq, "q")
+    kp, ks = _row_view(k, Hkv, "k")
+    vp_, vs = _row_view(v, Hkv, "v")
+    if ks != vs:
+        raise ValueError("k and v must share one row stride")
+    _need_contig(k_cache=k_cache, v_cache=v_cache, block_tables=block_tables, cu_q_lens=cu_q_lens,
+                 kv_lens=kv_lens, q_out=q_out, cos_cache=cos_cache, sin_cache=sin_cache)
+    shape = _shape_for(Hq, k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host, kv_lens_host,
+                       KERNEL_AUTO, k_scale, v_scale, v_cache)
+    if q_out is None:
+        q_out = torch.empty((q.shape[0], Hq, q.shape[2]), dtype=q.dtype, device=q.device)
+    rot = None
+    if rotary_dim:
+        rot = RpaRotary(cos_cache.data_ptr(), sin_cache.data_ptr(), cos_cache.shape[0],
+                        int(rotary_dim), int(bool(interleaved)))
+    _check(lib.rpa_rotary_write_kv(shape.ref, qp, kp, vp_, qs, ks,
+                                   None if rot is None else ctypes.byref(rot), _ptr(q_out),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(cu_q_lens), _ptr(kv_lens), _stream(q.device)))
+    return q_out
 
 
 def workspace_size(q, k_cache, block_tables, cu_q_lens_host, kv_lens_host, kernel=KERNEL_AUTO,

@@ -373,6 +373,84 @@ rpa_status rpa_write_kv(const rpa_shape *shape, const void *k_new, const void *v
   return st == RPA_OK ? ok() : st;
 }
 
+rpa_status rpa_rotary_write_kv(const rpa_shape *shape, const void *q, const void *k,
+                               const void *v, int64_t q_row_stride, int64_t kv_row_stride,
+                               const rpa_rotary *rotary, void *q_out, void *k_cache,
+                               void *v_cache, const int32_t *block_tables,
+                               const int32_t *cu_q_lens, const int32_t *kv_lens, void *stream) {
+  rpa_status st = validate(shape, true);
+  if (st != RPA_OK) return st;
+  const int Hq = shape->num_q_heads, Hkv = shape->num_kv_heads, D = shape->head_dim;
+  const int rd = rotary ? rotary->rotary_dim : 0;
+  if (rd < 0 || rd > D || rd % 16 != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rotary_dim %d must be 0 or a multiple of 16 <= head_dim %d",
+                rd, D);
+  if (rd > 0 && (!rotary->cos_cache || !rotary->sin_cache || rotary->max_position < 1))
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rotary tables are NULL or max_position %d < 1",
+                rotary->max_position);
+  if (q_row_stride < (int64_t)Hq * D || kv_row_stride < (int64_t)Hkv * D ||
+      q_row_stride % 8 != 0 || kv_row_stride % 8 != 0)
+    return fail(RPA_ERR_INVALID_ARGUMENT,
+                "row strides %lld (q) and %lld (k, v) must be multiples of 8 covering %d and %d "
+                "elements", (long long)q_row_stride, (long long)kv_row_stride, Hq * D, Hkv * D);
+  if (shape->total_q == 0) return ok();
+  if (!q || !k || !v || !q_out || !k_cache || !v_cache || !block_tables || !cu_q_lens || !kv_lens)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_rotary_write_kv: a device pointer is NULL");
+  for (const void *p : {q, k, v, static_cast<const void *>(q_out)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(RPA_ERR_INVALID_ARGUMENT, "q, k, v and q_out must be 16-byte aligned");
+  {  // q_out must not overlap q's rows (a split pair reads its partner from q)
+    const char *qb = static_cast<const char *>(q), *ob = static_cast<const char *>(q_out);
+    const int64_t T = shape->total_q;
+    const char *qe = qb + ((T - 1) * q_row_stride + (int64_t)Hq * D) * 2;
+    const char *oe = ob + T * (int64_t)Hq * D * 2;
+    if (qb < oe && ob < qe) return fail(RPA_ERR_INVALID_ARGUMENT, "q_out overlaps q");
+  }
+  for (int b = 0; b < shape->num_seqs; ++b) {
+    const int q_len = shape->h_cu_q_lens[b + 1] - shape->h_cu_q_lens[b];
+    if (q_len == 0) continue;
+    const int kv0 = kv_len_at(shape, b, 0);
+    if (shape->layout == RPA_LAYOUT_HEAD_MAJOR && rd > 0)
+      for (int g = 1; g < Hkv; ++g)
+        if (kv_len_at(shape, b, g) != kv0)
+          return fail(RPA_ERR_INVALID_ARGUMENT,
+                      "sequence %d: KV heads have different kv_lens; a rotated sequence needs one "
+                      "position per token", b);
+    if (rd > 0 && kv0 > rotary->max_position)
+      return fail(RPA_ERR_INVALID_ARGUMENT, "sequence %d reaches position %d >= max_position %d",
+                  b, kv0 - 1, rotary->max_position);
+  }
+  st = check_device();
+  if (st != RPA_OK) return st;
+  rpa::RotaryArgs r{};
+  r.q = static_cast<const uint16_t *>(q);
+  r.k = static_cast<const uint16_t *>(k);
+  r.v = static_cast<const uint16_t *>(v);
+  r.q_stride = q_row_stride;
+  r.kv_stride = kv_row_stride;
+  r.q_out = static_cast<uint16_t *>(q_out);
+  r.k_cache = static_cast<uint16_t *>(k_cache);
+  r.v_cache = static_cast<uint16_t *>(v_cache);
+  r.tables = block_tables;
+  r.cu_q_lens = cu_q_lens;
+  r.kv_lens = kv_lens;
+  r.cos_cache = rd > 0 ? rotary->cos_cache : nullptr;
+  r.sin_cache = rd > 0 ? rotary->sin_cache : nullptr;
+  r.B = shape->num_seqs;
+  r.T = shape->total_q;
+  r.Hq = Hq;
+  r.Hkv = Hkv;
+  r.rotary_dim = rd;
+  r.interleaved = rd > 0 && rotary->interleaved ? 1 : 0;
+  r.page_shift = ilog2(shape->page_size);
+  fill_layout(shape, r.page_stride, r.slot_stride, r.head_stride, r.bt_seq_stride,
+              r.bt_head_stride, r.kvl_seq_stride, r.kvl_head_stride);
+  fill_kv_dtype(r, shape->kv_dtype, shape->k_scale, shape->v_scale);
+  const hipError_t e = rpa::launch_rotary_write(r, D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "rotary write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t rpa_attention_workspace_size(const rpa_shape *shape) {
   if (validate(shape, true) != RPA_OK) return (size_t)-1;
   if (shape->total_q == 0) return 0;

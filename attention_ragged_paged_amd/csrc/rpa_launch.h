@@ -25,6 +25,25 @@ struct WriteArgs {
   float k_inv, v_inv;        // FP8: 1 / k_scale, 1 / v_scale
 };
 
+struct RotaryArgs {
+  const uint16_t *q, *k, *v;        // new rows, bf16; row t of head h at base + t*stride + h*D
+  int64_t q_stride, kv_stride;      // elements between consecutive tokens' rows
+  uint16_t *q_out;                  // [T][Hq][D] bf16
+  uint16_t *k_cache, *v_cache;
+  const int32_t *tables, *cu_q_lens, *kv_lens;
+  const float *cos_cache, *sin_cache;  // [max_position][rotary_dim / 2] fp32
+  int32_t B, T, Hq, Hkv;
+  int32_t rotary_dim, interleaved;  // rotary_dim: 0 or a multiple of 16, <= D
+  int32_t page_shift;
+  int64_t page_stride, slot_stride, head_stride;
+  int32_t bt_seq_stride, bt_head_stride;
+  int32_t kvl_seq_stride, kvl_head_stride;
+  int32_t kv8;
+  float k_inv, v_inv;
+};
+
+hipError_t launch_rotary_write(const RotaryArgs &r, int D, hipStream_t stream);
+
 enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };
 
 hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);

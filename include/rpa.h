@@ -116,6 +116,48 @@ rpa_status rpa_write_kv(const rpa_shape *shape, const void *k_new, const void *v
                         void *k_cache, void *v_cache, const int32_t *block_tables,
                         const int32_t *cu_q_lens, const int32_t *kv_lens, void *stream);
 
+/*
+ * Rotary embedding of the new tokens, fused with the scatter.  The ONNX Runtime
+ * PR rotates Q and K before scattering K/V (its rotary program, Phase 1b.2 commit
+ * note: position = past + local token, dims from rotary_dim on copied, V not
+ * rotated, interleaved or split pairs) and splits packed QKV first (its
+ * packed-QKV commit: per token Hq*D columns of Q, then Hkv*D of K, then Hkv*D of
+ * V).  Pair (x1, x2) at position p, pair index i becomes
+ *     (fmaf(x1, c, -(x2 * s)), fmaf(x2, c, x1 * s)),  c = cos_cache[p][i], s = sin_cache[p][i],
+ * in fp32, each rounded to bf16 (nearest even); interleaved pairs are dims
+ * (2i, 2i+1), split pairs (i, i + rotary_dim/2).
+ */
+typedef struct rpa_rotary {
+  const float *cos_cache;     /* device fp32 [max_position][rotary_dim / 2] */
+  const float *sin_cache;
+  int32_t max_position;       /* rows of the tables: every past + t must be below it */
+  int32_t rotary_dim;         /* 0 (no rotation) or a multiple of 16, <= head_dim */
+  int32_t interleaved;        /* 1: pairs (2i, 2i+1); 0: pairs (i, i + rotary_dim/2) */
+} rpa_rotary;
+
+/*
+ * rpa_rotary_write_kv -- rotate the new rows of Q and K and scatter K and V.
+ *   q, k, v       device bf16: row t of head h at q + t*q_row_stride + h*D
+ *                 (likewise k, v with kv_row_stride).  Packed QKV [T][(Hq+2Hkv)*D]
+ *                 is q = qkv, k = qkv + Hq*D, v = qkv + (Hq+Hkv)*D, both strides
+ *                 (Hq + 2*Hkv)*D; separate tensors have strides Hq*D and Hkv*D.
+ *                 Pointers and strides must be multiples of 8 elements.
+ *   rotary        NULL or rotary_dim 0: no rotation (a packed split + scatter)
+ *   q_out         device bf16 [T][Hq][D], the rotated Q (must not overlap q)
+ *   k_cache, v_cache, block_tables, cu_q_lens, kv_lens  as in rpa_write_kv: the
+ *                 rotated K and the V rows go to their page slots (FP8 caches
+ *                 store codes as defined at RPA_KV_FP8_E4M3).
+ * Position of token t of sequence b: kv_len - q_len_b + t.  For the KV-head-major
+ * layout every KV head of a rotated sequence must have the same kv_len (checked on
+ * the host mirrors).  Afterwards rpa_attention(q_out, ..., k_new = v_new = NULL)
+ * attends over the updated caches.  T == 0 returns RPA_OK.
+ */
+rpa_status rpa_rotary_write_kv(const rpa_shape *shape, const void *q, const void *k,
+                               const void *v, int64_t q_row_stride, int64_t kv_row_stride,
+                               const rpa_rotary *rotary, void *q_out, void *k_cache,
+                               void *v_cache, const int32_t *block_tables,
+                               const int32_t *cu_q_lens, const int32_t *kv_lens, void *stream);
+
 /* Bytes of device workspace rpa_attention needs for this shape (split-K
  * partials).  0 is a valid answer.  Returns (size_t)-1 on an invalid shape. */
 size_t rpa_attention_workspace_size(const rpa_shape *shape);

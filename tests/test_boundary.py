@@ -218,3 +218,33 @@ def test_graph_workspace_and_argument_checks(lib):
                                    None) == 1
     assert lib.rpa_graph_attention(ctypes.byref(s), p, p, p, p, p, p, 0.1, None, None, p, p, ws - 1,
                                    None) == 3
+
+
+def _rot(lib, s, rd=64, max_pos=64, qs=None, ks=None, tables=16, q=32, q_out=4096):
+    p = ctypes.c_void_p(16)
+    r = _rpa.RpaRotary(tables, tables, max_pos, rd, 0)
+    Hq, Hkv, D = s.num_q_heads, s.num_kv_heads, s.head_dim
+    return lib.rpa_rotary_write_kv(ctypes.byref(s), ctypes.c_void_p(q), p, p,
+                                   Hq * D if qs is None else qs, Hkv * D if ks is None else ks,
+                                   ctypes.byref(r), ctypes.c_void_p(q_out), p, p, p, p, p, None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(rd=24), "rotary_dim"),
+    (dict(rd=80), "rotary_dim"),
+    (dict(qs=100), "row strides"),
+    (dict(ks=64), "row strides"),
+    (dict(tables=0), "tables"),
+    (dict(max_pos=20), "max_position"),
+    (dict(q=32, q_out=48), "overlaps"),
+    (dict(q=40), "aligned"),
+])
+def test_rotary_argument_checks(lib, kw, frag):
+    s = _shape([0, 1, 3], [4, 30], D=64)
+    assert _rot(lib, s, **kw) == 1
+    assert frag in lib.rpa_last_error().decode()
+
+
+def test_rotary_head_major_needs_one_position_per_token(lib):
+    s = _shape([0, 1], [[4, 5]], layout=1)
+    assert _rot(lib, s) == 1 and "different kv_lens" in lib.rpa_last_error().decode()
