@@ -1062,7 +1062,8 @@ hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blo
 // One persistent launch that plans on the device.  Every workgroup reads the batch lengths
 // and derives, redundantly, the same plan the host planner derives from its mirrors
 // (decode-class sequences: q_len * G <= 16; KV split sizes cutting the work into about
-// target_items decode items and, for prefill-class work, about mixed_pf_items items beside
+// target_items decode items (decode_only_items when there is no prefill-class work) and, for
+// prefill-class work, about mixed_pf_items items beside
 // decode work or 8x fewer, 1024-key minimum, alone), with at most max_splits splits per
 // sequence.  Workgroup w runs item w first and then takes items from a queue; the last
 // workgroup to leave resets the queue and advances the call tag for the next call.
@@ -1186,7 +1187,9 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
   }
   GraphCall c;
   c.status = (uint32_t)bad;
-  c.split_dec = dec_units > 0 ? g_choose_split(dec_units, dec_long, 256, p.target_items, p.max_splits)
+  c.split_dec = dec_units > 0 ? g_choose_split(dec_units, dec_long, 256,
+                                               pf_units == 0 ? p.decode_only_items : p.target_items,
+                                               p.max_splits)
                               : (1 << 30);
   c.split_pf = pf_units == 0 ? (1 << 30)
                : dec_units > 0 ? g_choose_split(pf_units, pf_long, 512, p.mixed_pf_items, p.max_splits)
