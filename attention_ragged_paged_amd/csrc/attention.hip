@@ -175,8 +175,22 @@ __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
   return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits_dec(a, b);
 }
 
+// Item id of the decode stream -> (sequence, index within it) through a host-built order.
+__device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
+  if (id >= o.first[o.n]) return {-1, 0};
+  int lo = 0, hi = o.n;  // largest r < n with first[r] <= id
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (o.first[mid] <= id)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return {o.seq[lo], id - o.first[lo]};
+}
+
 template <int D, bool KV8>
-__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
+__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const DecodeOrder *order) {
   constexpr int KK = D / 32;     // 16x16x32 MFMAs per chunk for QK^T; load instructions per chunk
   constexpr int MB = D / 16;     // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
   constexpr int LPR = D / 8;     // lanes per 16-key row when loading
@@ -194,7 +208,9 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw) {
   const int lrow = KV8 ? lane / LPR8 : lane / LPR;
   const int lchk = KV8 ? lane % LPR8 : lane % LPR;
 
-  const ItemRef it = find_item(id, a.B, [&](int b) { return decode_count(a, b); });
+  const ItemRef it = order != nullptr && order->n > 0
+                         ? ordered_item(*order, id)
+                         : find_item(id, a.B, [&](int b) { return decode_count(a, b); });
   const int b = __builtin_amdgcn_readfirstlane(it.b);
   if (b < 0) return;
   const int q0 = a.cu_q_lens[b];
@@ -997,9 +1013,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
 #define RPA_DECODE_MIN_BLOCKS 2
 #endif
 template <int D, bool KV8>
-__global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a, DecodeOrder o) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
-  decode_item<D, KV8>(a, blockIdx.x, smem);
+  decode_item<D, KV8>(a, blockIdx.x, smem, &o);
 }
 
 template <int D, bool KV8>
@@ -1017,42 +1033,42 @@ constexpr size_t kMixedLds0Bytes =
     sizeof(DecodeSmem<D>) > (size_t)kPrefillBufBytes<D> ? sizeof(DecodeSmem<D>) : kPrefillBufBytes<D>;
 
 template <int D, bool KV8>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a, DecodeOrder o) {
   __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
   __shared__ int last;
   if ((int)blockIdx.x < a.n_pf_items)
     prefill_item<D, KV8>(a, blockIdx.x, lds0, lds1, &last);
   else
-    decode_item<D, KV8>(a, blockIdx.x - a.n_pf_items, lds0);
+    decode_item<D, KV8>(a, blockIdx.x - a.n_pf_items, lds0, &o);
 }
 
 template <int D, bool KV8>
-static hipError_t launch_attention_d(const AttnArgs &a, AttnKernel kind, int n_blocks,
-                                     hipStream_t stream) {
+static hipError_t launch_attention_d(const AttnArgs &a, const DecodeOrder &o, AttnKernel kind,
+                                     int n_blocks, hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_blocks), block(kThreads);
   switch (kind) {
     case AttnKernel::kDecode:
-      hipLaunchKernelGGL((decode_kernel<D, KV8>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<D, KV8>), grid, block, 0, stream, a, o);
       break;
     case AttnKernel::kPrefill:
       hipLaunchKernelGGL((prefill_kernel<D, KV8>), grid, block, 0, stream, a);
       break;
     case AttnKernel::kMixed:
-      hipLaunchKernelGGL((mixed_kernel<D, KV8>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((mixed_kernel<D, KV8>), grid, block, 0, stream, a, o);
       break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
-                            hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs &a, const DecodeOrder &o, int D, AttnKernel kind,
+                            int n_blocks, hipStream_t stream) {
   if (D == 128)
-    return a.kv8 ? launch_attention_d<128, true>(a, kind, n_blocks, stream)
-                 : launch_attention_d<128, false>(a, kind, n_blocks, stream);
-  return a.kv8 ? launch_attention_d<64, true>(a, kind, n_blocks, stream)
-               : launch_attention_d<64, false>(a, kind, n_blocks, stream);
+    return a.kv8 ? launch_attention_d<128, true>(a, o, kind, n_blocks, stream)
+                 : launch_attention_d<128, false>(a, o, kind, n_blocks, stream);
+  return a.kv8 ? launch_attention_d<64, true>(a, o, kind, n_blocks, stream)
+               : launch_attention_d<64, false>(a, o, kind, n_blocks, stream);
 }
 
 }  // namespace rpa
@@ -1266,7 +1282,7 @@ __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, Graph
   // to that kind (a shared loop measured ~20% slower per decode item).
   if (c.n_pf_items == 0) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
-      decode_item<D, KV8>(a, item, lds0);
+      decode_item<D, KV8>(a, item, lds0, nullptr);
   } else if (c.n_pf_items == c.n_items) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
       prefill_item<D, KV8>(a, item, lds0, lds1, &last);
@@ -1275,7 +1291,7 @@ __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, Graph
       if (item < c.n_pf_items)
         prefill_item<D, KV8>(a, item, lds0, lds1, &last);
       else
-        decode_item<D, KV8>(a, item - c.n_pf_items, lds0);
+        decode_item<D, KV8>(a, item - c.n_pf_items, lds0, nullptr);
     }
   }
   // Leaving: the queue and tag accesses of this workgroup are complete (their values were

@@ -528,7 +528,46 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   a.pf_tokens = p.pf_tokens;
   a.n_pf_items = p.n_pf_items;
   a.pf_counter_base = (int32_t)wl.pf_counter_base;
-  hipError_t e = rpa::launch_attention(a, shape->head_dim, kind, p.n_pf_items + p.n_dec_items, hs);
+  // Decode items longest first (a launch that ends on its shortest items has the shortest tail).
+  rpa::DecodeOrder order;
+  order.n = 0;
+  if (p.n_dec_items > 0) {
+    const int G = a.G;
+    int idx[rpa::kMaxOrderedSeqs];
+    int len[rpa::kMaxOrderedSeqs];
+    int n = 0;
+    for (int b = 0; b < shape->num_seqs && n <= rpa::kMaxOrderedSeqs; ++b) {
+      const int q_len = shape->h_cu_q_lens[b + 1] - shape->h_cu_q_lens[b];
+      if (q_len == 0 || !decode_class(p, q_len, G)) continue;
+      if (n == rpa::kMaxOrderedSeqs) {
+        n = rpa::kMaxOrderedSeqs + 1;  // too many: keep the in-kernel sequence order
+        break;
+      }
+      const int maxkv = max_kv_len_host(shape, b);
+      const int ns = splits_of(p, q_len, G, maxkv);
+      idx[n] = b;
+      len[n] = cdiv(cdiv(maxkv, ns), 64) * 64;  // keys per item (the kernels' even split)
+      ++n;
+    }
+    if (n <= rpa::kMaxOrderedSeqs) {
+      int perm[rpa::kMaxOrderedSeqs];
+      for (int i = 0; i < n; ++i) perm[i] = i;
+      std::stable_sort(perm, perm + n, [&](int x, int y) { return len[x] > len[y]; });
+      int first = 0;
+      for (int i = 0; i < n; ++i) {
+        const int b = idx[perm[i]];
+        const int q_len = shape->h_cu_q_lens[b + 1] - shape->h_cu_q_lens[b];
+        order.seq[i] = b;
+        order.first[i] = first;
+        first += shape->num_kv_heads * cdiv(q_len * G, rpa::kDecodeRows) *
+                 splits_of(p, q_len, G, max_kv_len_host(shape, b));
+      }
+      order.first[n] = first;
+      order.n = n;
+    }
+  }
+  hipError_t e = rpa::launch_attention(a, order, shape->head_dim, kind,
+                                       p.n_pf_items + p.n_dec_items, hs);
   if (e != hipSuccess) return fail(RPA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -48,10 +48,22 @@ enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };
 
 hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 
+// The order in which decode items are handed to workgroups, built on the host from the
+// length mirrors: decode-class sequences listed by decreasing item length (longest first, so
+// the launch ends on its shortest items), with the first item of each.  Passed as a kernel
+// argument; n = 0 maps items in sequence order with the in-kernel scan instead (batches with
+// more decode-class sequences than fit, and the graph-capturable call).
+constexpr int kMaxOrderedSeqs = 256;
+struct DecodeOrder {
+  int32_t n;
+  int32_t first[kMaxOrderedSeqs + 1];  // first[n] = number of decode items
+  int32_t seq[kMaxOrderedSeqs];
+};
+
 // Runs the attention kernel of the given kind on n_blocks workgroups (the prefill items,
 // then the decode stream's workgroups).
-hipError_t launch_attention(const AttnArgs &a, int D, AttnKernel kind, int n_blocks,
-                            hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, const DecodeOrder &order, int D, AttnKernel kind,
+                            int n_blocks, hipStream_t stream);
 
 struct GraphPlan;
 
