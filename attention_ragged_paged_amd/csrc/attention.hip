@@ -175,7 +175,8 @@ __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
   return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits_dec(a, b);
 }
 
-// Item id of the decode stream -> (sequence, index within it) through a host-built order.
+// Item id of the decode stream -> (rank in a host-built order, index within the sequence);
+// rank -1 past the last item.
 __device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
   if (id >= o.first[o.n]) return {-1, 0};
   int lo = 0, hi = o.n;  // largest r < n with first[r] <= id
@@ -186,7 +187,7 @@ __device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
     else
       hi = mid;
   }
-  return {o.seq[lo], id - o.first[lo]};
+  return {lo, id - o.first[lo]};
 }
 
 template <int D, bool KV8>
@@ -208,24 +209,34 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Dec
   const int lrow = KV8 ? lane / LPR8 : lane / LPR;
   const int lchk = KV8 ? lane % LPR8 : lane % LPR;
 
-  const ItemRef it = order != nullptr && order->n > 0
-                         ? ordered_item(*order, id)
-                         : find_item(id, a.B, [&](int b) { return decode_count(a, b); });
-  const int b = __builtin_amdgcn_readfirstlane(it.b);
-  if (b < 0) return;
-  const int q0 = a.cu_q_lens[b];
-  const int q_len = a.cu_q_lens[b + 1] - q0;
+  int b, q0, q_len, max_kv;
+  ItemRef it;
+  if (order != nullptr && order->n > 0) {  // everything from the kernel arguments
+    it = ordered_item(*order, id);
+    if (it.b < 0) return;
+    b = order->seq[it.b];
+    q0 = order->q0[it.b];
+    q_len = order->q_len[it.b];
+    max_kv = order->kv[it.b];
+  } else {
+    it = find_item(id, a.B, [&](int bb) { return decode_count(a, bb); });
+    b = __builtin_amdgcn_readfirstlane(it.b);
+    if (b < 0) return;
+    q0 = a.cu_q_lens[b];
+    q_len = a.cu_q_lens[b + 1] - q0;
+    max_kv = max_kv_len(a, b);
+  }
   const int n_rt = ceil_div(q_len * a.G, kDecodeRows);
-  const int nsplit = num_splits_dec(a, b);
+  const int nsplit = max(1, ceil_div(max_kv, a.split_dec));
   int rem = __builtin_amdgcn_readfirstlane(it.rem);
   const int s = rem % nsplit;
   rem /= nsplit;
   const int rt = rem % n_rt;
   const int g = rem / n_rt;
-  const int kv_len = kv_len_of(a, b, g);
+  const int kv_len = a.kvl_head_stride == 0 ? max_kv : kv_len_of(a, b, g);  // per head if head-major
   const int past = kv_len - q_len;
   const int n_rows = q_len * a.G;
-  const int split = even_split(max_kv_len(a, b), nsplit);
+  const int split = even_split(max_kv, nsplit);
   const int k_begin = s * split;
   const int k_end = min(min(kv_len, k_begin + split), dec_item_kend(kv_len, q_len, a.G, rt));
   const bool fused = a.k_new != nullptr;

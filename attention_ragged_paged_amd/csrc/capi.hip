@@ -558,6 +558,9 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
         const int b = idx[perm[i]];
         const int q_len = shape->h_cu_q_lens[b + 1] - shape->h_cu_q_lens[b];
         order.seq[i] = b;
+        order.q0[i] = shape->h_cu_q_lens[b];
+        order.q_len[i] = q_len;
+        order.kv[i] = max_kv_len_host(shape, b);
         order.first[i] = first;
         first += shape->num_kv_heads * cdiv(q_len * G, rpa::kDecodeRows) *
                  splits_of(p, q_len, G, max_kv_len_host(shape, b));

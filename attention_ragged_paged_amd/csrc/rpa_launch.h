@@ -53,11 +53,16 @@ hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 // the launch ends on its shortest items), with the first item of each.  Passed as a kernel
 // argument; n = 0 maps items in sequence order with the in-kernel scan instead (batches with
 // more decode-class sequences than fit, and the graph-capturable call).
-constexpr int kMaxOrderedSeqs = 256;
+// Each listed sequence also carries its start, length and longest kv_len, so an item needs no
+// load before its query and table loads.
+constexpr int kMaxOrderedSeqs = 160;  // keeps the kernel arguments under 4 KB
 struct DecodeOrder {
   int32_t n;
   int32_t first[kMaxOrderedSeqs + 1];  // first[n] = number of decode items
   int32_t seq[kMaxOrderedSeqs];
+  int32_t q0[kMaxOrderedSeqs];         // cu_q_lens[seq]
+  int32_t q_len[kMaxOrderedSeqs];
+  int32_t kv[kMaxOrderedSeqs];         // longest kv_len over the sequence's KV heads
 };
 
 // Runs the attention kernel of the given kind on n_blocks workgroups (the prefill items,
