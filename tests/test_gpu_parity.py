@@ -256,3 +256,20 @@ def test_long_context_mixed_splits():
     say("long-context mixed splits")
     b = wl.ragged_batch("lcm", [300, 1, 1, 1], [40300, 9001, 101, 70001], 32, 8, 128, 16, 7500, 81)
     _sampled(b, 160, "long-context mixed")
+
+
+@pytest.mark.parametrize("n_seqs", [160, 161, 300])
+def test_many_decode_sequences_order_and_scan(n_seqs):
+    """Up to 160 decode-class sequences the decode items follow a host-built longest-first
+    order carried in the kernel arguments; beyond that the in-kernel scan maps them.  Both
+    sides of the limit, and a mixed batch, against the oracle on sampled rows."""
+    say(f"{n_seqs} decode sequences")
+    rng = np.random.default_rng(n_seqs)
+    kv = rng.integers(1, 700, size=n_seqs)
+    q = np.ones(n_seqs, np.int64)
+    pool = int(((kv + 15) // 16).sum()) + 48
+    b = wl.ragged_batch("many", q, kv, 8, 2, 128, 16, pool, 71, max_pages=48)
+    _sampled(b, 300, f"{n_seqs} decodes")
+    q[0], kv[0] = 40, 640   # one prefill chunk makes it a mixed batch
+    b2 = wl.ragged_batch("many_mixed", q, kv, 8, 2, 128, 16, pool, 72, max_pages=48)
+    _sampled(b2, 300, f"{n_seqs} mixed")
