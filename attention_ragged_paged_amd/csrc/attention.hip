@@ -175,6 +175,22 @@ __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
   return a.Hkv * ceil_div(q_len * a.G, kDecodeRows) * num_splits_dec(a, b);
 }
 
+// Graph-capturable calls order decode items without a host: sequences fall into length
+// classes of their items (longest first), items follow class by class, and within a class
+// the sequence order.  dec_first[k] is the first decode item of class k.
+constexpr int kDecClasses = 4;
+struct DecodeClasses {
+  int dec_first[kDecClasses + 1];
+  int split;  // the call's decode split size
+};
+
+__device__ __forceinline__ int dec_class(int max_kv, int split) {
+  const int ns = max(1, ceil_div(max_kv, split));
+  const long long len = even_split(max_kv, ns);  // keys per item
+  const long long sp = split;
+  return 4 * len > 3 * sp ? 0 : 2 * len > sp ? 1 : 4 * len > sp ? 2 : 3;
+}
+
 // Item id of the decode stream -> (rank in a host-built order, index within the sequence);
 // rank -1 past the last item.
 __device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
@@ -191,7 +207,8 @@ __device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
 }
 
 template <int D, bool KV8>
-__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const DecodeOrder *order) {
+__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const DecodeOrder *order,
+                            const DecodeClasses *classes = nullptr) {
   constexpr int KK = D / 32;     // 16x16x32 MFMAs per chunk for QK^T; load instructions per chunk
   constexpr int MB = D / 16;     // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
   constexpr int LPR = D / 8;     // lanes per 16-key row when loading
@@ -218,6 +235,21 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Dec
     q0 = order->q0[it.b];
     q_len = order->q_len[it.b];
     max_kv = order->kv[it.b];
+  } else if (classes != nullptr) {  // class by class, then sequence order
+    if (id >= classes->dec_first[kDecClasses]) return;
+    int k = 0;
+#pragma unroll
+    for (int kk = 1; kk < kDecClasses; ++kk)
+      if (classes->dec_first[kk] <= id) k = kk;
+    it = find_item(id - classes->dec_first[k], a.B, [&](int bb) {
+      const int n = decode_count(a, bb);
+      return n > 0 && dec_class(max_kv_len(a, bb), classes->split) == k ? n : 0;
+    });
+    b = __builtin_amdgcn_readfirstlane(it.b);
+    if (b < 0) return;
+    q0 = a.cu_q_lens[b];
+    q_len = a.cu_q_lens[b + 1] - q0;
+    max_kv = max_kv_len(a, b);
   } else {
     it = find_item(id, a.B, [&](int bb) { return decode_count(a, bb); });
     b = __builtin_amdgcn_readfirstlane(it.b);
@@ -1108,6 +1140,7 @@ __device__ __forceinline__ int g_choose_split(long long units, int longest_kv, i
 struct GraphCall {
   uint32_t status;
   int split_dec, split_pf, n_pf_items, n_items;
+  DecodeClasses classes;  // decode items class by class (longest items first)
 };
 
 // Workgroup-wide reduction scratch of the planning step (not shared with the items' LDS).
@@ -1115,7 +1148,7 @@ struct PlanScratch {
   long long units[kThreads / 64][2];  // decode, prefill 64-key units
   int longest[kThreads / 64][2];      // longest kv_len of each class
   int bad[kThreads / 64];
-  long long items[kThreads / 64][2];  // decode, prefill items
+  long long items[kThreads / 64][kDecClasses + 1];  // decode items per class, prefill items
 };
 
 // Wave-wide reduction of non-negative 32-bit values with DPP moves (no LDS round trips):
@@ -1221,13 +1254,18 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
   c.split_pf = pf_units == 0 ? (1 << 30)
                : dec_units > 0 ? g_choose_split(pf_units, pf_long, 512, p.mixed_pf_items, p.max_splits)
                                : g_choose_split(pf_units * 8, pf_long, 1024, p.target_items, p.max_splits);
-  long long n_dec = 0, n_pf = 0;
+  long long n_cls[kDecClasses] = {0, 0, 0, 0}, n_pf = 0;
   auto count_items = [&](int q_len, int kv) {
     if (q_len <= 0) return;
-    if (is_dec(q_len))
-      n_dec += (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
-    else
+    if (is_dec(q_len)) {
+      const long long n = (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
+      const int k = dec_class(kv, c.split_dec);
+#pragma unroll
+      for (int kk = 0; kk < kDecClasses; ++kk)
+        if (kk == k) n_cls[kk] += n;
+    } else {
       n_pf += (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * max(1, ceil_div(kv, c.split_pf));
+    }
   };
   if (tid < p.B) count_items(q0, kv0);
   for (int b = tid + kThreads; b < p.B; b += kThreads) {
@@ -1235,24 +1273,34 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
     seq(b, q_len, kv);
     count_items(q_len, kv);
   }
-  n_dec = wave_sum64(n_dec);
+#pragma unroll
+  for (int kk = 0; kk < kDecClasses; ++kk) n_cls[kk] = wave_sum64(n_cls[kk]);
   n_pf = wave_sum64(n_pf);
   if (lane_id() == 0) {
-    red.items[wave][0] = n_dec;
-    red.items[wave][1] = n_pf;
+#pragma unroll
+    for (int kk = 0; kk < kDecClasses; ++kk) red.items[wave][kk] = n_cls[kk];
+    red.items[wave][kDecClasses] = n_pf;
   }
   __syncthreads();
-  n_dec = n_pf = 0;
+  long long n_dec = 0;
+  n_pf = 0;
+  c.classes.dec_first[0] = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    n_dec += red.items[w][0];
-    n_pf += red.items[w][1];
+  for (int kk = 0; kk < kDecClasses; ++kk) {
+    long long nk = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) nk += red.items[w][kk];
+    n_dec += nk;
+    c.classes.dec_first[kk + 1] = __builtin_amdgcn_readfirstlane((int)n_dec);
   }
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) n_pf += red.items[w][kDecClasses];
   c.n_pf_items = bad ? 0 : (int)n_pf;
   c.n_items = bad ? 0 : (int)(n_pf + n_dec);
   // Every lane holds the same plan: keep it in scalar registers.
   c.status = __builtin_amdgcn_readfirstlane(c.status);
   c.split_dec = __builtin_amdgcn_readfirstlane(c.split_dec);
+  c.classes.split = c.split_dec;
   c.split_pf = __builtin_amdgcn_readfirstlane(c.split_pf);
   c.n_pf_items = __builtin_amdgcn_readfirstlane(c.n_pf_items);
   c.n_items = __builtin_amdgcn_readfirstlane(c.n_items);
@@ -1293,7 +1341,7 @@ __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, Graph
   // to that kind (a shared loop measured ~20% slower per decode item).
   if (c.n_pf_items == 0) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
-      decode_item<D, KV8>(a, item, lds0, nullptr);
+      decode_item<D, KV8>(a, item, lds0, nullptr, &c.classes);
   } else if (c.n_pf_items == c.n_items) {
     for (int item = blockIdx.x; item < c.n_items; item = next_item())
       prefill_item<D, KV8>(a, item, lds0, lds1, &last);
@@ -1302,7 +1350,7 @@ __global__ __launch_bounds__(kThreads, 2) void graph_kernel(AttnArgs args, Graph
       if (item < c.n_pf_items)
         prefill_item<D, KV8>(a, item, lds0, lds1, &last);
       else
-        decode_item<D, KV8>(a, item - c.n_pf_items, lds0, nullptr);
+        decode_item<D, KV8>(a, item - c.n_pf_items, lds0, nullptr, &c.classes);
     }
   }
   // Leaving: the queue and tag accesses of this workgroup are complete (their values were
