@@ -9,8 +9,10 @@
 // is that page's seqlens_q fix: token t of a sequence sits at position past + t and sees
 // keys 0 .. past + t.
 //
-// One launch per call.  The kernels map blocks onto work with in-kernel scans over the
-// sequences (find_item, dec_locate), so no work list is built or uploaded.  A row is one
+// One launch per call.  The kernels map blocks onto work items themselves: prefill items
+// with an in-kernel scan over the sequences (find_item), decode items through an order the
+// host builds from its length mirrors and passes in the kernel arguments (longest items
+// first), or the same scan when no order is passed; nothing is uploaded.  A row is one
 // (token, query head) pair; the G query heads of a GQA group are packed into the same item
 // so every K/V byte is read once per group.
 //
