@@ -239,11 +239,14 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Dec
     max_kv = order->kv[it.b];
   } else if (classes != nullptr) {  // class by class, then sequence order
     if (id >= classes->dec_first[kDecClasses]) return;
-    int k = 0;
+    int k = 0, base = 0;  // (no indexing by k: that would put the classes in scratch memory)
 #pragma unroll
     for (int kk = 1; kk < kDecClasses; ++kk)
-      if (classes->dec_first[kk] <= id) k = kk;
-    it = find_item(id - classes->dec_first[k], a.B, [&](int bb) {
+      if (classes->dec_first[kk] <= id) {
+        k = kk;
+        base = classes->dec_first[kk];
+      }
+    it = find_item(id - base, a.B, [&](int bb) {
       const int n = decode_count(a, bb);
       return n > 0 && dec_class(max_kv_len(a, bb), classes->split) == k ? n : 0;
     });
@@ -791,18 +794,19 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     for (int u = 0; u < NR8; ++u) {
       const int g0 = min(kt0 + RPW8 * (4 * u + w), k_end - 1);  // rows past the range repeat
       const int key = min(g0 + lr8, k_end - 1);                  // the range's last key
-      if (fused && key >= past) {
-        const int64_t noff = new_row0 + (int64_t)key * new_stride + 16 * c16;
-        kst[2 * u] = *reinterpret_cast<const u32x4 *>(a.k_new + noff);
-        kst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(a.k_new + noff + 8);
-        vst[2 * u] = *reinterpret_cast<const u32x4 *>(a.v_new + noff);
-        vst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(a.v_new + noff + 8);
-      } else {
-        const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
-        const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
-        kst[2 * u] = *reinterpret_cast<const u32x4 *>(kc8 + off);
-        vst[2 * u] = *reinterpret_cast<const u32x4 *>(vc8 + off);
-      }
+      // Every lane loads twice, from addresses chosen per lane (no branch): a cached row's 16
+      // codes (the second load repeats the first, a cache hit), or a new row's 16 bf16 values.
+      const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+      const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
+      const int64_t noff = new_row0 + (int64_t)key * new_stride + 16 * c16;
+      const bool is_new = fused && key >= past;
+      const uint8_t *k0 = is_new ? reinterpret_cast<const uint8_t *>(a.k_new + noff) : kc8 + off;
+      const uint8_t *v0 = is_new ? reinterpret_cast<const uint8_t *>(a.v_new + noff) : vc8 + off;
+      const int step = is_new ? 16 : 0;
+      kst[2 * u] = *reinterpret_cast<const u32x4 *>(k0);
+      kst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(k0 + step);
+      vst[2 * u] = *reinterpret_cast<const u32x4 *>(v0);
+      vst[2 * u + 1] = *reinterpret_cast<const u32x4 *>(v0 + step);
     }
   };
   auto commit8 = [&](int tile, auto par) {
@@ -1204,15 +1208,16 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
   int bad = tid < p.B && seq(tid, q0, kv0) ? 4 : 0;
   long long dec_units = 0, pf_units = 0;
   int dec_long = 0, pf_long = 0;
+  // (selects, not branches: branches here made the compiler keep the accumulators in an
+  // indexed scratch array)
   auto count_units = [&](int q_len, int kv) {
-    if (q_len <= 0) return;
-    if (is_dec(q_len)) {
-      dec_units += (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * ceil_div(kv, 64);
-      dec_long = max(dec_long, kv);
-    } else {
-      pf_units += (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * ceil_div(kv, 64);
-      pf_long = max(pf_long, kv);
-    }
+    const bool live = q_len > 0, dec = is_dec(q_len);
+    const long long du = (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * ceil_div(kv, 64);
+    const long long pu = (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * ceil_div(kv, 64);
+    dec_units += live && dec ? du : 0;
+    pf_units += live && !dec ? pu : 0;
+    dec_long = live && dec ? max(dec_long, kv) : dec_long;
+    pf_long = live && !dec ? max(pf_long, kv) : pf_long;
   };
   if (tid < p.B) count_units(q0, kv0);
   for (int b = tid + kThreads; b < p.B; b += kThreads) {
@@ -1258,16 +1263,13 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
                                : g_choose_split(pf_units * 8, pf_long, 1024, p.target_items, p.max_splits);
   long long n_cls[kDecClasses] = {0, 0, 0, 0}, n_pf = 0;
   auto count_items = [&](int q_len, int kv) {
-    if (q_len <= 0) return;
-    if (is_dec(q_len)) {
-      const long long n = (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
-      const int k = dec_class(kv, c.split_dec);
+    const bool live = q_len > 0, dec = is_dec(q_len);
+    const long long nd = (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
+    const long long np = (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * max(1, ceil_div(kv, c.split_pf));
+    const int k = dec_class(kv, c.split_dec);
 #pragma unroll
-      for (int kk = 0; kk < kDecClasses; ++kk)
-        if (kk == k) n_cls[kk] += n;
-    } else {
-      n_pf += (long long)p.Hkv * ceil_div(q_len, p.pf_tokens) * max(1, ceil_div(kv, c.split_pf));
-    }
+    for (int kk = 0; kk < kDecClasses; ++kk) n_cls[kk] += live && dec && kk == k ? nd : 0;
+    n_pf += live && !dec ? np : 0;
   };
   if (tid < p.B) count_items(q0, kv0);
   for (int b = tid + kThreads; b < p.B; b += kThreads) {
