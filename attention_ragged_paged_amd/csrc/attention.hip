@@ -9,10 +9,11 @@
 // is that page's seqlens_q fix: token t of a sequence sits at position past + t and sees
 // keys 0 .. past + t.
 //
-// One launch per call.  The kernels map blocks onto work items themselves: prefill items
-// with an in-kernel scan over the sequences (find_item), decode items through an order the
-// host builds from its length mirrors and passes in the kernel arguments (longest items
-// first), or the same scan when no order is passed; nothing is uploaded.  A row is one
+// One launch per call.  The kernels map blocks onto work items themselves, through an order
+// of sequences the host builds from its length mirrors and passes in the kernel arguments
+// (decode items longest first; a prefill launch's items in sequence order), or with an
+// in-kernel scan over the sequences (find_item) when no order is passed, as for the prefill
+// items of a mixed launch; nothing is uploaded.  A row is one
 // (token, query head) pair; the G query heads of a GQA group are packed into the same item
 // so every K/V byte is read once per group.
 //
@@ -193,9 +194,9 @@ __device__ __forceinline__ int dec_class(int max_kv, int split) {
   return 4 * len > 3 * sp ? 0 : 2 * len > sp ? 1 : 4 * len > sp ? 2 : 3;
 }
 
-// Item id of the decode stream -> (rank in a host-built order, index within the sequence);
-// rank -1 past the last item.
-__device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
+// Item id -> (rank in a host-built order, index within the sequence); rank -1 past the last
+// item.
+__device__ __forceinline__ ItemRef ordered_item(const SeqOrder &o, int id) {
   if (id >= o.first[o.n]) return {-1, 0};
   int lo = 0, hi = o.n;  // largest r < n with first[r] <= id
   while (hi - lo > 1) {
@@ -209,7 +210,7 @@ __device__ __forceinline__ ItemRef ordered_item(const DecodeOrder &o, int id) {
 }
 
 template <int D, bool KV8>
-__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const DecodeOrder *order,
+__device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const SeqOrder *order,
                             const DecodeClasses *classes = nullptr) {
   constexpr int KK = D / 32;     // 16x16x32 MFMAs per chunk for QK^T; load instructions per chunk
   constexpr int MB = D / 16;     // 16x16x16 MFMAs per chunk for PV (16-dim output blocks)
@@ -598,7 +599,8 @@ template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
 template <int D, bool KV8>
-__device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, int *last_flag) {
+__device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, int *last_flag,
+                             const SeqOrder *order = nullptr) {
   constexpr int KS = D / 16;                                // QK^T MFMAs per 32-key block
   constexpr int MD = D / 32;                                // PV output blocks of 32 dims
   constexpr int kChunks = D / 8;                            // 16-byte chunks per row
@@ -612,23 +614,35 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   const int r32 = lane & 31;
   const int hf = lane >> 5;
 
-  const ItemRef it = find_item(id, a.B, [&](int b) { return prefill_count<D>(a, b); });
-  const int b = __builtin_amdgcn_readfirstlane(it.b);
-  if (b < 0) return;
-  const int q0 = a.cu_q_lens[b];
-  const int q_len = a.cu_q_lens[b + 1] - q0;
+  ItemRef it;
+  int b, q0, q_len, max_kv;
+  if (order != nullptr && order->n > 0) {  // everything from the kernel arguments
+    it = ordered_item(*order, id);
+    if (it.b < 0) return;
+    b = order->seq[it.b];
+    q0 = order->q0[it.b];
+    q_len = order->q_len[it.b];
+    max_kv = order->kv[it.b];
+  } else {
+    it = find_item(id, a.B, [&](int bb) { return prefill_count<D>(a, bb); });
+    b = __builtin_amdgcn_readfirstlane(it.b);
+    if (b < 0) return;
+    q0 = a.cu_q_lens[b];
+    q_len = a.cu_q_lens[b + 1] - q0;
+    max_kv = max_kv_len(a, b);
+  }
   const int n_qt = ceil_div(q_len, a.pf_tokens);
-  const int nsplit = num_splits_pf(a, b);
+  const int nsplit = max(1, ceil_div(max_kv, a.split_pf));  // as num_splits_pf
   int rem = __builtin_amdgcn_readfirstlane(it.rem);
   const int s = rem % nsplit;
   rem /= nsplit;
   const int g = rem % a.Hkv;
   const int qt = n_qt - 1 - rem / a.Hkv;  // heaviest (latest) query tiles first
-  const int kv_len = kv_len_of(a, b, g);
+  const int kv_len = a.kvl_head_stride == 0 ? max_kv : kv_len_of(a, b, g);  // per head if head-major
   const int past = kv_len - q_len;
   const int t_first = qt * a.pf_tokens;
   const int t_last = min(q_len - 1, t_first + a.pf_tokens - 1);
-  const int split = even_split(max_kv_len(a, b), nsplit);
+  const int split = even_split(max_kv, nsplit);
   const int k_begin = s * split;
   const int k_end = min(min(kv_len, k_begin + split), past + t_last + 1);
   const int n_tiles = k_end > k_begin ? ceil_div(k_end - k_begin, kPrefillKeys) : 0;
@@ -1062,17 +1076,17 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
 #define RPA_DECODE_MIN_BLOCKS 2
 #endif
 template <int D, bool KV8>
-__global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a, DecodeOrder o) {
+__global__ __launch_bounds__(kThreads, RPA_DECODE_MIN_BLOCKS) void decode_kernel(AttnArgs a, SeqOrder o) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   decode_item<D, KV8>(a, blockIdx.x, smem, &o);
 }
 
 template <int D, bool KV8>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a, SeqOrder o) {
   __shared__ __attribute__((aligned(16))) char lds0[kPrefillBufBytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
   __shared__ int last;
-  prefill_item<D, KV8>(a, blockIdx.x, lds0, lds1, &last);
+  prefill_item<D, KV8>(a, blockIdx.x, lds0, lds1, &last, &o);
 }
 
 // One launch for a batch holding both kinds: prefill items first (they are the longest),
@@ -1082,7 +1096,7 @@ constexpr size_t kMixedLds0Bytes =
     sizeof(DecodeSmem<D>) > (size_t)kPrefillBufBytes<D> ? sizeof(DecodeSmem<D>) : kPrefillBufBytes<D>;
 
 template <int D, bool KV8>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a, DecodeOrder o) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a, SeqOrder o) {
   __shared__ __attribute__((aligned(16))) char lds0[kMixedLds0Bytes<D>];
   __shared__ __attribute__((aligned(16))) char lds1[kPrefillBufBytes<D>];
   __shared__ int last;
@@ -1093,7 +1107,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(AttnArgs a, DecodeOr
 }
 
 template <int D, bool KV8>
-static hipError_t launch_attention_d(const AttnArgs &a, const DecodeOrder &o, AttnKernel kind,
+static hipError_t launch_attention_d(const AttnArgs &a, const SeqOrder &o, AttnKernel kind,
                                      int n_blocks, hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_blocks), block(kThreads);
@@ -1102,7 +1116,7 @@ static hipError_t launch_attention_d(const AttnArgs &a, const DecodeOrder &o, At
       hipLaunchKernelGGL((decode_kernel<D, KV8>), grid, block, 0, stream, a, o);
       break;
     case AttnKernel::kPrefill:
-      hipLaunchKernelGGL((prefill_kernel<D, KV8>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<D, KV8>), grid, block, 0, stream, a, o);
       break;
     case AttnKernel::kMixed:
       hipLaunchKernelGGL((mixed_kernel<D, KV8>), grid, block, 0, stream, a, o);
@@ -1111,7 +1125,7 @@ static hipError_t launch_attention_d(const AttnArgs &a, const DecodeOrder &o, At
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs &a, const DecodeOrder &o, int D, AttnKernel kind,
+hipError_t launch_attention(const AttnArgs &a, const SeqOrder &o, int D, AttnKernel kind,
                             int n_blocks, hipStream_t stream) {
   if (D == 128)
     return a.kv8 ? launch_attention_d<128, true>(a, o, kind, n_blocks, stream)

@@ -536,10 +536,33 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   a.pf_tokens = p.pf_tokens;
   a.n_pf_items = p.n_pf_items;
   a.pf_counter_base = (int32_t)wl.pf_counter_base;
-  // Decode items longest first (a launch that ends on its shortest items has the shortest tail).
-  rpa::DecodeOrder order;
+  // Decode items longest first (a launch that ends on its shortest items has the shortest tail);
+  // a prefill launch's sequences in their own order (the in-kernel scan's numbering), so that
+  // its items load no lengths before their query and table loads.
+  rpa::SeqOrder order;
   order.n = 0;
-  if (p.n_dec_items > 0) {
+  if (kind == rpa::AttnKernel::kPrefill) {
+    const int G = a.G;
+    int n = 0, first = 0;
+    for (int b = 0; b < shape->num_seqs; ++b) {
+      const int q_len = shape->h_cu_q_lens[b + 1] - shape->h_cu_q_lens[b];
+      if (q_len == 0 || decode_class(p, q_len, G)) continue;
+      if (n == rpa::kMaxOrderedSeqs) {
+        n = 0;  // too many: the in-kernel scan
+        break;
+      }
+      const int maxkv = max_kv_len_host(shape, b);
+      order.seq[n] = b;
+      order.q0[n] = shape->h_cu_q_lens[b];
+      order.q_len[n] = q_len;
+      order.kv[n] = maxkv;
+      order.first[n] = first;
+      first += shape->num_kv_heads * cdiv(q_len, p.pf_tokens) * splits_of(p, q_len, G, maxkv);
+      ++n;
+    }
+    order.first[n] = first;
+    order.n = n;
+  } else if (p.n_dec_items > 0) {
     const int G = a.G;
     int idx[rpa::kMaxOrderedSeqs];
     int len[rpa::kMaxOrderedSeqs];

@@ -48,17 +48,19 @@ enum class AttnKernel { kDecode = 1, kPrefill = 2, kMixed = 3 };
 
 hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 
-// The order in which decode items are handed to workgroups, built on the host from the
-// length mirrors: decode-class sequences listed by decreasing item length (longest first, so
-// the launch ends on its shortest items), with the first item of each.  Passed as a kernel
-// argument; n = 0 maps items in sequence order with the in-kernel scan instead (batches with
-// more decode-class sequences than fit, and the graph-capturable call).
-// Each listed sequence also carries its start, length and longest kv_len, so an item needs no
-// load before its query and table loads.
+// The sequences of one class whose items a launch hands out, built on the host from the
+// length mirrors, with the first item of each.  Decode-class sequences are listed by
+// decreasing item length (longest first, so the launch ends on its shortest items);
+// prefill-class sequences of a prefill launch in sequence order (each one's items already run
+// heaviest query tile first).  Passed as a kernel argument; n = 0 maps items in sequence
+// order with the in-kernel scan instead (batches with more sequences of the class than fit,
+// the prefill items of a mixed launch, and the graph-capturable call).  Each listed sequence
+// also carries its start, length and longest kv_len, so an item needs no load before its
+// query and table loads.
 constexpr int kMaxOrderedSeqs = 160;  // keeps the kernel arguments under 4 KB
-struct DecodeOrder {
+struct SeqOrder {
   int32_t n;
-  int32_t first[kMaxOrderedSeqs + 1];  // first[n] = number of decode items
+  int32_t first[kMaxOrderedSeqs + 1];  // first[n] = number of items
   int32_t seq[kMaxOrderedSeqs];
   int32_t q0[kMaxOrderedSeqs];         // cu_q_lens[seq]
   int32_t q_len[kMaxOrderedSeqs];
@@ -66,8 +68,9 @@ struct DecodeOrder {
 };
 
 // Runs the attention kernel of the given kind on n_blocks workgroups (the prefill items,
-// then the decode stream's workgroups).
-hipError_t launch_attention(const AttnArgs &a, const DecodeOrder &order, int D, AttnKernel kind,
+// then the decode stream's workgroups); the order lists the decode-class sequences of a
+// decode or mixed launch and the prefill-class ones of a prefill launch.
+hipError_t launch_attention(const AttnArgs &a, const SeqOrder &order, int D, AttnKernel kind,
                             int n_blocks, hipStream_t stream);
 
 struct GraphPlan;
