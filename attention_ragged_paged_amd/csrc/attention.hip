@@ -51,11 +51,32 @@ __device__ __forceinline__ int table_at(const AttnArgs &a, int b, int g, int log
 }
 
 // Split partials travel between workgroups (possibly on different XCDs, each with its own
-// L2) through device-coherent accesses: device-scope relaxed atomic stores and loads, which
-// are written through and read past the non-coherent L2 (sc1).  The writer waits for its
-// stores to complete before it arrives on the counter, and the reader loads only after
-// its arrival returned last, so no cache-wide writeback or invalidate is ever needed
-// (a device-scope fence would flush the whole L2 of the XCD).
+// L2) through device-coherent accesses, which are written through and read past the
+// non-coherent L2 (cache policy sc1).  The writer waits for its stores to complete before it
+// arrives on the counter, and the reader loads only after its arrival returned last, so no
+// cache-wide writeback or invalidate is ever needed (a device-scope fence would flush the
+// whole L2 of the XCD).  Output rows move 16 bytes a lane through a buffer resource over the
+// item's first partial row (a wave-uniform base; lane offsets stay far below 2 GiB), so that
+// a row's partial goes out in whole 16-byte pieces; the (max, sum) pairs use device-scope
+// relaxed atomic stores and loads, which carry the same policy.
+constexpr int kCoherent = 16;  // buffer cache-policy operand: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rows(const float *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void st_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                              const f32x4 &v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0,
+                                         kCoherent);
+}
+
+__device__ __forceinline__ f32x4 ld_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0,
+                                                                         kCoherent));
+}
+
 __device__ __forceinline__ void st_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -64,13 +85,14 @@ __device__ __forceinline__ float ld_coherent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void st_coherent4(float *p, const f32x4 &v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st_coherent(p + i, v[i]);
+// Partial output row (split s, token, head) lives at part_o + ((s T + token) Hq + head) D.
+// An item's rows: tokens tok0 .., heads h0 .. of the same split; its base and a row's offset:
+__device__ __forceinline__ const float *partial_base(const AttnArgs &a, int s, int tok0, int h0,
+                                                     int D) {
+  return a.part_o + (((int64_t)s * a.T + tok0) * a.Hq + h0) * D;
 }
-
-__device__ __forceinline__ f32x4 ld_coherent4(const float *p) {
-  return f32x4{ld_coherent(p), ld_coherent(p + 1), ld_coherent(p + 2), ld_coherent(p + 3)};
+__device__ __forceinline__ uint32_t partial_off(const AttnArgs &a, int dtok, int dh, int d, int D) {
+  return (uint32_t)(((dtok * a.Hq + dh) * D + d) * 4);
 }
 
 // Waits until every memory access this wave issued has completed.
@@ -93,7 +115,9 @@ __device__ __forceinline__ unsigned arrive(unsigned long long *p, unsigned long 
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), online over batches of 4 splits whose
 // loads are all issued before any is used.
 template <int D, int NPT>
-__device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int token, int h, int d0) {
+__device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int token, int h, int d0,
+                                          int tok0, int h0) {
+  const uint32_t off = partial_off(a, token - tok0, h - h0, d0, D);
   float M = kNegInf, L = 0.f;
   f32x4 o[NPT / 4];
 #pragma unroll
@@ -106,8 +130,10 @@ __device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int tok
       const int64_t pr = ((int64_t)min(s0 + u, nsplit - 1) * a.T + token) * a.Hq + h;
       mv[u] = ld_coherent(a.part_ml + pr * 2);
       lv[u] = ld_coherent(a.part_ml + pr * 2 + 1);
+      const __amdgpu_buffer_rsrc_t rows =
+          coherent_rows(partial_base(a, min(s0 + u, nsplit - 1), tok0, h0, D));
 #pragma unroll
-      for (int q = 0; q < NPT / 4; ++q) ov[u][q] = ld_coherent4(a.part_o + pr * D + d0 + 4 * q);
+      for (int q = 0; q < NPT / 4; ++q) ov[u][q] = ld_coherent16(rows, off + 16 * q);
     }
     float Mn = M;
 #pragma unroll
@@ -547,10 +573,15 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
           u32x2{pack_bf16x2(o[q][0] * inv, o[q][1] * inv), pack_bf16x2(o[q][2] * inv, o[q][3] * inv)};
     return;
   }
+  // the item's rows: tokens q0 + (rt 16) / G .., heads g G .. (uniform base, per-row offsets)
+  const int tok0 = q0 + rt * kDecodeRows / a.G;
+  const int h0 = g * a.G;
   if (out_ok) {
     const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h;
+    const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, s, tok0, h0, D));
+    const uint32_t off = partial_off(a, token - tok0, h - h0, d0, D);
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q) st_coherent4(a.part_o + prow * D + d0 + 4 * q, o[q]);
+    for (int q = 0; q < DPT / 4; ++q) st_coherent16(rows, off + 16 * q, o[q]);
     if (d0 == 0) {
       st_coherent(a.part_ml + prow * 2 + 0, M);
       st_coherent(a.part_ml + prow * 2 + 1, L);
@@ -565,7 +596,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   }
   __syncthreads();
   if (!sm.last || !out_ok) return;
-  merge_row<D, DPT>(a, nsplit, token, h, d0);
+  merge_row<D, DPT>(a, nsplit, token, h, d0, tok0, h0);
 }
 
 // =========================================================================== prefill ======
@@ -1036,16 +1067,20 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       }
     return;
   }
+  // the item's rows: tokens q0 + t_first .., heads g G .. (uniform base, per-row offsets)
+  const int tok0 = q0 + t_first;
+  const int h0 = g * a.G;
   if (row_ok) {
     const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h_row;
-    float *po = a.part_o + prow * D;
+    const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, s, tok0, h0, D));
+    const uint32_t off = partial_off(a, t_row - t_first, hg, 0, D);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         const int d = 32 * md + 8 * vq + 4 * hf;
-        st_coherent4(po + d, f32x4{acc[md][4 * vq], acc[md][4 * vq + 1], acc[md][4 * vq + 2],
-                                   acc[md][4 * vq + 3]});
+        st_coherent16(rows, off + 4 * d, f32x4{acc[md][4 * vq], acc[md][4 * vq + 1],
+                                               acc[md][4 * vq + 2], acc[md][4 * vq + 3]});
       }
     if (hf == 0) {
       st_coherent(a.part_ml + prow * 2 + 0, m_run);
@@ -1067,7 +1102,8 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   const int mt = t_first + mrow % a.pf_tokens;
   if (mhg >= a.G || mt >= q_len) return;
 #pragma unroll 1
-  for (int d = 0; d < DH; d += 16) merge_row<D, 16>(a, nsplit, q0 + mt, g * a.G + mhg, (tid & 1) * DH + d);
+  for (int d = 0; d < DH; d += 16)
+    merge_row<D, 16>(a, nsplit, q0 + mt, g * a.G + mhg, (tid & 1) * DH + d, tok0, h0);
 }
 
 // =========================================================================== kernels ======
