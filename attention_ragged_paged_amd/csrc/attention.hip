@@ -1178,9 +1178,8 @@ hipError_t launch_attention(const AttnArgs &a, const SeqOrder &o, int D, AttnKer
 // and derives, redundantly, the same plan the host planner derives from its mirrors
 // (decode-class sequences: q_len * G <= 16; KV split sizes cutting the work into about
 // target_items decode items (decode_only_items when there is no prefill-class work) and, for
-// prefill-class work, about mixed_pf_items items beside
-// decode work or 8x fewer, 1024-key minimum, alone), with at most max_splits splits per
-// sequence.  Workgroup w runs item w first and then takes items from a queue; the last
+// prefill-class work, about mixed_pf_items items beside decode work or target_items / 4 items
+// (1024-key minimum) alone), with at most max_splits splits per sequence.  Workgroup w runs item w first and then takes items from a queue; the last
 // workgroup to leave resets the queue and advances the call tag for the next call.
 namespace rpa {
 
@@ -1310,7 +1309,7 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
                               : (1 << 30);
   c.split_pf = pf_units == 0 ? (1 << 30)
                : dec_units > 0 ? g_choose_split(pf_units, pf_long, 512, p.mixed_pf_items, p.max_splits)
-                               : g_choose_split(pf_units * 8, pf_long, 1024, p.target_items, p.max_splits);
+                               : g_choose_split(pf_units * 4, pf_long, 1024, p.target_items, p.max_splits);
   long long n_cls[kDecClasses] = {0, 0, 0, 0}, n_pf = 0;
   auto count_items = [&](int q_len, int kv) {
     const bool live = q_len > 0, dec = is_dec(q_len);
