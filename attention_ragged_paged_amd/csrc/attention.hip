@@ -1177,9 +1177,9 @@ hipError_t launch_attention(const AttnArgs &a, const SeqOrder &o, int D, AttnKer
 // One persistent launch that plans on the device.  Every workgroup reads the batch lengths
 // and derives, redundantly, the same plan the host planner derives from its mirrors
 // (decode-class sequences: q_len * G <= 16; KV split sizes cutting the work into about
-// target_items decode items (decode_only_items when there is no prefill-class work) and, for
-// prefill-class work, about mixed_pf_items items beside decode work or target_items / 4 items
-// (1024-key minimum) alone), with at most max_splits splits per sequence.  Workgroup w runs item w first and then takes items from a queue; the last
+// mixed_dec_items decode items beside prefill-class work or decode_only_items alone, and
+// about mixed_pf_items prefill items beside decode work or prefill_only_items (1024-key
+// minimum) alone), with at most max_splits splits per sequence.  Workgroup w runs item w first and then takes items from a queue; the last
 // workgroup to leave resets the queue and advances the call tag for the next call.
 namespace rpa {
 
@@ -1304,12 +1304,12 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
   GraphCall c;
   c.status = (uint32_t)bad;
   c.split_dec = dec_units > 0 ? g_choose_split(dec_units, dec_long, 256,
-                                               pf_units == 0 ? p.decode_only_items : p.target_items,
+                                               pf_units == 0 ? p.decode_only_items : p.mixed_dec_items,
                                                p.max_splits)
                               : (1 << 30);
   c.split_pf = pf_units == 0 ? (1 << 30)
                : dec_units > 0 ? g_choose_split(pf_units, pf_long, 512, p.mixed_pf_items, p.max_splits)
-                               : g_choose_split(pf_units * 4, pf_long, 1024, p.target_items, p.max_splits);
+                               : g_choose_split(pf_units, pf_long, 1024, p.prefill_only_items, p.max_splits);
   long long n_cls[kDecClasses] = {0, 0, 0, 0}, n_pf = 0;
   auto count_items = [&](int q_len, int kv) {
     const bool live = q_len > 0, dec = is_dec(q_len);

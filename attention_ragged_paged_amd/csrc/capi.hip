@@ -67,32 +67,35 @@ constexpr int kDecodeRowsMax = 16;
 constexpr int kMaxSplits = 64;
 // Work items the split sizes aim for: a few workgroups per compute unit of the 256-CU chip.
 // Fewer, longer items amortise each item's fixed cost (work lookup, first loads, combine,
-// split merge); even splits keep the tail short.
-#ifndef RPA_TARGET_ITEMS
-#define RPA_TARGET_ITEMS 1024
-#endif
-constexpr long long kTargetItems = RPA_TARGET_ITEMS;
-// A decode-only batch aims at fewer, longer items than the decode share of a mixed batch
-// (measured on llama3_decode: 768 items 2-3% faster than 1024 with bf16 and FP8 caches; the
-// mixed batch, whose decode items share the chip with long prefill items, prefers 1024).
+// split merge); even splits keep the tail short.  Measured on one MI355X:
+// - a decode-only batch: llama3_decode 768 items 2-3% faster than 512, 896 or 1024 (bf16 and
+//   FP8 caches);
 #ifndef RPA_DECODE_ONLY_ITEMS
 #define RPA_DECODE_ONLY_ITEMS 768
 #endif
 constexpr long long kDecodeOnlyItems = RPA_DECODE_ONLY_ITEMS;
-// In a mixed batch the prefill-class items run beside the decode items, which keep the
-// memory system busy; splitting them further only adds partial traffic and merges, and when
-// they outnumber a fraction of the workgroup slots they crowd the decode items out.  They
-// are cut into about this many items.
+// - the decode share of a mixed batch, whose decode items run beside long prefill items:
+//   mixed_chunked 1280 items 1.2% faster than 1024 (1536: bf16 faster still, FP8 slower);
+#ifndef RPA_MIXED_DEC_ITEMS
+#define RPA_MIXED_DEC_ITEMS 1280
+#endif
+constexpr long long kMixedDecodeItems = RPA_MIXED_DEC_ITEMS;
+// - the prefill share of a mixed batch: those items run beside the decode items, which keep
+//   the memory system busy; splitting them further only adds partial traffic and merges, and
+//   when they outnumber a fraction of the workgroup slots they crowd the decode items out
+//   (mixed_chunked: 128 items 375 us, 192 items 404 us; mixed_chunked_fp8: 128 items 240 us,
+//   160 or 192 items 278 us);
 #ifndef RPA_MIXED_PF_ITEMS
 #define RPA_MIXED_PF_ITEMS 128
 #endif
 constexpr long long kMixedPrefillItems = RPA_MIXED_PF_ITEMS;
-// Over an FP8 cache the prefill tiles go through registers and take longer, so the chunk is
-// cut finer (mixed_chunked_fp8: 192 items 325 us, 128 items 351 us; bf16 prefers 128).
-#ifndef RPA_MIXED_PF_ITEMS_FP8
-#define RPA_MIXED_PF_ITEMS_FP8 192
+// - a prefill-only batch, compute-bound, is split only when it has too few items to fill the
+//   chip (one 512-token chunk at context 8192, alone: 128 items 210 us, 256 items 145 us,
+//   512 items 148 us, 1024 items 254 us).
+#ifndef RPA_PREFILL_ONLY_ITEMS
+#define RPA_PREFILL_ONLY_ITEMS 256
 #endif
-constexpr long long kMixedPrefillItemsFp8 = RPA_MIXED_PF_ITEMS_FP8;
+constexpr long long kPrefillOnlyItems = RPA_PREFILL_ONLY_ITEMS;
 
 int kv_len_at(const rpa_shape *s, int b, int g) {
   return s->layout == RPA_LAYOUT_SEQ_MAJOR ? s->h_kv_lens[b]
@@ -226,7 +229,7 @@ int splits_of(const Plan &p, int q_len, int G, int maxkv) {
 
 // A split size in keys (a multiple of 64) that cuts `units` 64-key units into about
 // `target` items, never giving one sequence more than kMaxSplits splits.
-int choose_split(long long units, int longest_kv, int min_keys, long long target = kTargetItems) {
+int choose_split(long long units, int longest_kv, int min_keys, long long target) {
   long long per_item = std::max<long long>(1, (units + target - 1) / target);
   long long split = std::max<long long>(per_item * 64, min_keys);
   const long long floor_for_cap = (long long)cdiv(cdiv(longest_kv, 64), kMaxSplits) * 64;
@@ -271,18 +274,11 @@ Plan make_plan(const rpa_shape *s) {
   }
   if (dec_units > 0)
     p.split_dec = choose_split(dec_units, dec_longest, 256,
-                               pf_units == 0 ? kDecodeOnlyItems : kTargetItems);
+                               pf_units == 0 ? kDecodeOnlyItems : kMixedDecodeItems);
   if (pf_units > 0) {
-    if (kind == RPA_KERNEL_PREFILL)
-      // A prefill-only batch is compute-bound: split only when it has too few items to fill
-      // the chip, aiming at about a quarter of kTargetItems (prefill items hold 8x the rows of
-      // decode ones).  Measured on one 512-token chunk at context 8192, alone: 128 items
-      // 210 us, 256 items 145 us, 512 items 148 us, 1024 items 254 us.
-      p.split_pf = choose_split(pf_units * 4, pf_longest, 1024);
-    else
-      p.split_pf = choose_split(pf_units, pf_longest, 512,
-                                s->kv_dtype == RPA_KV_FP8_E4M3 ? kMixedPrefillItemsFp8
-                                                               : kMixedPrefillItems);
+    p.split_pf = kind == RPA_KERNEL_PREFILL
+                     ? choose_split(pf_units, pf_longest, 1024, kPrefillOnlyItems)
+                     : choose_split(pf_units, pf_longest, 512, kMixedPrefillItems);
   }
   for (int b = 0; b < s->num_seqs; ++b) {
     const int q_len = s->h_cu_q_lens[b + 1] - s->h_cu_q_lens[b];
@@ -763,10 +759,10 @@ rpa_status rpa_graph_attention(const rpa_graph_shape *shape, const void *q, void
   pa.kvl_head_stride = a.kvl_head_stride;
   pa.pf_tokens = a.pf_tokens;
   pa.max_splits = shape->max_splits;
-  pa.target_items = (int32_t)kTargetItems;
   pa.decode_only_items = (int32_t)kDecodeOnlyItems;
-  pa.mixed_pf_items =
-      (int32_t)(shape->kv_dtype == RPA_KV_FP8_E4M3 ? kMixedPrefillItemsFp8 : kMixedPrefillItems);
+  pa.mixed_dec_items = (int32_t)kMixedDecodeItems;
+  pa.mixed_pf_items = (int32_t)kMixedPrefillItems;
+  pa.prefill_only_items = (int32_t)kPrefillOnlyItems;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = rpa::launch_graph_attention(a, pa, shape->head_dim, workgroup_slots(), hs);
   if (e != hipSuccess) return fail(RPA_ERR_HIP, "graph attention launch: %s", hipGetErrorString(e));

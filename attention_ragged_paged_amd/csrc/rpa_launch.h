@@ -83,8 +83,9 @@ struct GraphPlanArgs {
   int32_t page_size, max_pages;
   int32_t kvl_seq_stride, kvl_head_stride;
   int32_t pf_tokens, max_splits;
-  int32_t target_items, mixed_pf_items;  // the host planner's item targets
-  int32_t decode_only_items;
+  // the host planner's item targets: decode-only batch; decode and prefill shares of a mixed
+  // batch; prefill-only batch
+  int32_t decode_only_items, mixed_dec_items, mixed_pf_items, prefill_only_items;
 };
 
 // Persistent attention of a graph-capturable call on n_workgroups workgroups: each derives
