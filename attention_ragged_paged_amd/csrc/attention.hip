@@ -111,20 +111,22 @@ __device__ __forceinline__ unsigned arrive(unsigned long long *p, unsigned long 
   }
 }
 
-// Merge the nsplit partials of one output row (dims d0 .. d0 + NPT) and write bf16:
+// Merge the nsplit partials of one output row and write bf16: the thread's dims are the
+// 16-byte chunks c + 16 q, q < D/64, so that the 16 threads of a row touch whole rows;
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), online over batches of 4 splits whose
 // loads are all issued before any is used.
-template <int D, int NPT>
-__device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int token, int h, int d0,
+template <int D>
+__device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int token, int h, int c,
                                           int tok0, int h0) {
-  const uint32_t off = partial_off(a, token - tok0, h - h0, d0, D);
+  constexpr int NQ = D / 64;  // chunks per thread
+  const uint32_t off = partial_off(a, token - tok0, h - h0, 4 * c, D);
   float M = kNegInf, L = 0.f;
-  f32x4 o[NPT / 4];
+  f32x4 o[NQ];
 #pragma unroll
-  for (int q = 0; q < NPT / 4; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NQ; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += 4) {
     float mv[4], lv[4];
-    f32x4 ov[4][NPT / 4];
+    f32x4 ov[4][NQ];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t pr = ((int64_t)min(s0 + u, nsplit - 1) * a.T + token) * a.Hq + h;
@@ -133,7 +135,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int tok
       const __amdgpu_buffer_rsrc_t rows =
           coherent_rows(partial_base(a, min(s0 + u, nsplit - 1), tok0, h0, D));
 #pragma unroll
-      for (int q = 0; q < NPT / 4; ++q) ov[u][q] = ld_coherent16(rows, off + 16 * q);
+      for (int q = 0; q < NQ; ++q) ov[u][q] = ld_coherent16(rows, off + 256 * q);
     }
     float Mn = M;
 #pragma unroll
@@ -143,22 +145,22 @@ __device__ __forceinline__ void merge_row(const AttnArgs &a, int nsplit, int tok
     const float sc = fast_exp2(M - Mu);
     L *= sc;
 #pragma unroll
-    for (int q = 0; q < NPT / 4; ++q) o[q] = o[q] * sc;
+    for (int q = 0; q < NQ; ++q) o[q] = o[q] * sc;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (s0 + u >= nsplit) continue;
       const float wv = fast_exp2(mv[u] - Mu);
       L += lv[u] * wv;
 #pragma unroll
-      for (int q = 0; q < NPT / 4; ++q) o[q] += ov[u][q] * wv;
+      for (int q = 0; q < NQ; ++q) o[q] += ov[u][q] * wv;
     }
     M = Mn;
   }
   const float inv = a.out_scale / L;
-  uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
+  uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + 4 * c;
 #pragma unroll
-  for (int q = 0; q < NPT / 4; ++q)
-    *reinterpret_cast<u32x2 *>(op + 4 * q) =
+  for (int q = 0; q < NQ; ++q)
+    *reinterpret_cast<u32x2 *>(op + 64 * q) =
         u32x2{pack_bf16x2(o[q][0] * inv, o[q][1] * inv), pack_bf16x2(o[q][2] * inv, o[q][3] * inv)};
 }
 
@@ -539,25 +541,26 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
     for (int i4 = 0; i4 < 4; ++i4) sm.o[w][r16][16 * mb + 4 * j + i4] = acc[mb][i4];
   __syncthreads();
 
-  // Combine the 4 waves: thread -> (row, D/16 consecutive dims).
-  constexpr int DPT = D / 16;
+  // Combine the 4 waves: thread -> (row, 16-byte chunks c + 16 q of the row), so that the
+  // 16 threads of a row read, store and merge whole rows.
+  constexpr int NQ = D / 64;
   const int row = tid >> 4;
-  const int d0 = (tid & 15) * DPT;
+  const int c = tid & 15;
   float M = kNegInf;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm.m[ww][row]);
   const float M_use = M == kNegInf ? 0.f : M;
   float L = 0.f;
-  f32x4 o[DPT / 4];
+  f32x4 o[NQ];
 #pragma unroll
-  for (int q = 0; q < DPT / 4; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NQ; ++q) o[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
     const float wv = fast_exp2(sm.m[ww][row] - M_use);
     L += sm.l[ww][row] * wv;
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q)
-      o[q] += *reinterpret_cast<const f32x4 *>(&sm.o[ww][row][d0 + 4 * q]) * wv;
+    for (int q = 0; q < NQ; ++q)
+      o[q] += *reinterpret_cast<const f32x4 *>(&sm.o[ww][row][4 * c + 64 * q]) * wv;
   }
   const int frow = rt * kDecodeRows + row;
   const bool out_ok = frow < n_rows;
@@ -566,10 +569,10 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   if (nsplit == 1) {
     if (!out_ok) return;
     const float inv = a.out_scale / L;
-    uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + d0;
+    uint16_t *op = a.out + ((int64_t)token * a.Hq + h) * D + 4 * c;
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q)
-      *reinterpret_cast<u32x2 *>(op + 4 * q) =
+    for (int q = 0; q < NQ; ++q)
+      *reinterpret_cast<u32x2 *>(op + 64 * q) =
           u32x2{pack_bf16x2(o[q][0] * inv, o[q][1] * inv), pack_bf16x2(o[q][2] * inv, o[q][3] * inv)};
     return;
   }
@@ -579,10 +582,10 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   if (out_ok) {
     const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h;
     const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, s, tok0, h0, D));
-    const uint32_t off = partial_off(a, token - tok0, h - h0, d0, D);
+    const uint32_t off = partial_off(a, token - tok0, h - h0, 4 * c, D);
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q) st_coherent16(rows, off + 16 * q, o[q]);
-    if (d0 == 0) {
+    for (int q = 0; q < NQ; ++q) st_coherent16(rows, off + 256 * q, o[q]);
+    if (c == 0) {
       st_coherent(a.part_ml + prow * 2 + 0, M);
       st_coherent(a.part_ml + prow * 2 + 1, L);
     }
@@ -596,7 +599,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   }
   __syncthreads();
   if (!sm.last || !out_ok) return;
-  merge_row<D, DPT>(a, nsplit, token, h, d0, tok0, h0);
+  merge_row<D>(a, nsplit, token, h, c, tok0, h0);
 }
 
 // =========================================================================== prefill ======
@@ -1067,24 +1070,45 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       }
     return;
   }
-  // the item's rows: tokens q0 + t_first .., heads g G .. (uniform base, per-row offsets)
+  // The item's rows: tokens q0 + t_first .., heads g G .. (uniform base, per-row offsets).
+  // The partial goes out whole rows at a time: each wave's rows are staged in LDS (free once
+  // the last tile is done; rows 0..63 in the first buffer, 64..127 in the second, 16-byte
+  // chunks swizzled by the row), then lane l of a group of CH = D/4 lanes stores chunk l of
+  // one row, so every write-through store covers whole lines.
   const int tok0 = q0 + t_first;
   const int h0 = g * a.G;
-  if (row_ok) {
-    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h_row;
-    const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, s, tok0, h0, D));
-    const uint32_t off = partial_off(a, t_row - t_first, hg, 0, D);
+  constexpr int CH = D / 4;             // 16-byte chunks per row
+  constexpr int RPS = kThreads / CH;    // rows per workgroup-wide step
+  auto stage_row = [&](int row) {
+    return reinterpret_cast<float *>(row < 64 ? lds0 : lds1) + (row & 63) * D;
+  };
+  {
+    float *st = stage_row(rr);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
-        const int d = 32 * md + 8 * vq + 4 * hf;
-        st_coherent16(rows, off + 4 * d, f32x4{acc[md][4 * vq], acc[md][4 * vq + 1],
-                                               acc[md][4 * vq + 2], acc[md][4 * vq + 3]});
+        const int c = 8 * md + 2 * vq + hf;  // dims 4c .. 4c+3 = 32 md + 8 vq + 4 hf
+        *reinterpret_cast<f32x4 *>(st + 4 * (c ^ (rr & (CH - 1)))) =
+            f32x4{acc[md][4 * vq], acc[md][4 * vq + 1], acc[md][4 * vq + 2], acc[md][4 * vq + 3]};
       }
-    if (hf == 0) {
-      st_coherent(a.part_ml + prow * 2 + 0, m_run);
-      st_coherent(a.part_ml + prow * 2 + 1, l_run);
+  }
+  if (row_ok && hf == 0) {
+    const int64_t prow = ((int64_t)s * a.T + token) * a.Hq + h_row;
+    st_coherent(a.part_ml + prow * 2 + 0, m_run);
+    st_coherent(a.part_ml + prow * 2 + 1, l_run);
+  }
+  __syncthreads();
+  const int lc = tid % CH;  // this lane's chunk
+  {
+    const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, s, tok0, h0, D));
+#pragma unroll
+    for (int i = 0; i < kPrefillRows / RPS; ++i) {
+      const int row = i * RPS + tid / CH;
+      const int rt = row % a.pf_tokens, rhg = row / a.pf_tokens;
+      if (rhg < a.G && t_first + rt < q_len)
+        st_coherent16(rows, partial_off(a, rt, rhg, 4 * lc, D),
+                      *reinterpret_cast<const f32x4 *>(stage_row(row) + 4 * (lc ^ (row & (CH - 1)))));
     }
   }
   // Arrive; the last of the nsplit items of this (query tile, KV head) merges all partials.
@@ -1096,14 +1120,71 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   }
   __syncthreads();
   if (!*last_flag) return;
-  constexpr int DH = D / 2;  // two threads per row, half of D each, 16 dims per pass
-  const int mrow = tid >> 1;
-  const int mhg = mrow / a.pf_tokens;
-  const int mt = t_first + mrow % a.pf_tokens;
-  if (mhg >= a.G || mt >= q_len) return;
+  // Merge, whole rows again: kRB rows per lane group in flight, splits in batches of 4 whose
+  // loads are all issued before any is used.
+  constexpr int kRB = 4;
 #pragma unroll 1
-  for (int d = 0; d < DH; d += 16)
-    merge_row<D, 16>(a, nsplit, q0 + mt, g * a.G + mhg, (tid & 1) * DH + d, tok0, h0);
+  for (int i0 = 0; i0 < kPrefillRows / RPS; i0 += kRB) {
+    float M[kRB], L[kRB];
+    f32x4 o[kRB];
+    int rt[kRB], rhg[kRB];
+    bool ok[kRB];
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+      const int row = (i0 + j) * RPS + tid / CH;
+      rt[j] = row % a.pf_tokens;
+      rhg[j] = row / a.pf_tokens;
+      ok[j] = rhg[j] < a.G && t_first + rt[j] < q_len;
+      M[j] = kNegInf;
+      L[j] = 0.f;
+      o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float mv[kRB][4], lv[kRB][4];
+      f32x4 ov[kRB][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int su = min(s0 + u, nsplit - 1);
+        const __amdgpu_buffer_rsrc_t rows = coherent_rows(partial_base(a, su, tok0, h0, D));
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+          // rows past the item read its first row (always valid); their results are dropped
+          const int jt = ok[j] ? rt[j] : 0, jh = ok[j] ? rhg[j] : 0;
+          const int64_t pr = ((int64_t)su * a.T + tok0 + jt) * a.Hq + h0 + jh;
+          mv[j][u] = ld_coherent(a.part_ml + pr * 2);
+          lv[j][u] = ld_coherent(a.part_ml + pr * 2 + 1);
+          ov[j][u] = ld_coherent16(rows, partial_off(a, jt, jh, 4 * lc, D));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRB; ++j) {
+        float Mn = M[j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[j][u]);
+        const float Mu = Mn == kNegInf ? 0.f : Mn;
+        const float sc = fast_exp2(M[j] - Mu);
+        L[j] *= sc;
+        o[j] = o[j] * sc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (s0 + u >= nsplit) continue;
+          const float wv = fast_exp2(mv[j][u] - Mu);
+          L[j] += lv[j][u] * wv;
+          o[j] += ov[j][u] * wv;
+        }
+        M[j] = Mn;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+      if (!ok[j]) continue;
+      const float inv = a.out_scale / L[j];
+      uint16_t *op = a.out + ((int64_t)(tok0 + rt[j]) * a.Hq + h0 + rhg[j]) * D + 4 * lc;
+      *reinterpret_cast<u32x2 *>(op) =
+          u32x2{pack_bf16x2(o[j][0] * inv, o[j][1] * inv), pack_bf16x2(o[j][2] * inv, o[j][3] * inv)};
+    }
+  }
 }
 
 // =========================================================================== kernels ======

@@ -90,10 +90,10 @@ constexpr long long kMixedDecodeItems = RPA_MIXED_DEC_ITEMS;
 #endif
 constexpr long long kMixedPrefillItems = RPA_MIXED_PF_ITEMS;
 // - a prefill-only batch, compute-bound, is split only when it has too few items to fill the
-//   chip (one 512-token chunk at context 8192, alone: 128 items 210 us, 256 items 145 us,
-//   512 items 148 us, 1024 items 254 us).
+//   chip (one 512-token chunk at context 8192, alone: 128 items 210 us, 256 items 129 us,
+//   512 items 102 us, 1024 items 136 us).
 #ifndef RPA_PREFILL_ONLY_ITEMS
-#define RPA_PREFILL_ONLY_ITEMS 256
+#define RPA_PREFILL_ONLY_ITEMS 512
 #endif
 constexpr long long kPrefillOnlyItems = RPA_PREFILL_ONLY_ITEMS;
 
