@@ -251,6 +251,20 @@ def test_long_context_prefill_splits():
     _sampled(b, 160, "long-context prefill")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(24, 8, 64), (16, 2, 64), (8, 8, 128), (12, 4, 128)])
+def test_prefill_split_rows_every_group_size(Hq, Hkv, D):
+    """A lone chunk at a long context, prefill-only, so its few items are cut into KV splits
+    whose partials are written and merged as whole rows: group sizes 1, 3 and 8 (rows of a
+    128-row item that fall past the group or the chunk stay unwritten), both head dims, every
+    output element against the oracle."""
+    say(f"prefill split rows Hq={Hq} Hkv={Hkv} D={D}")
+    b = wl.ragged_batch("psr", [90], [6090], Hq, Hkv, D, 32, 200, 82 + Hq)
+    d = Dev(b)
+    assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_PREFILL
+    del d
+    _full_check(b, label=f"prefill split rows {Hq}/{Hkv}/{D}")
+
+
 def test_long_context_mixed_splits():
     """Mixed batch with a chunk at a 40k context and decodes up to 70k keys."""
     say("long-context mixed splits")
