@@ -209,7 +209,7 @@ __device__ __forceinline__ int decode_count(const AttnArgs &a, int b) {
 // Graph-capturable calls order decode items without a host: sequences fall into length
 // classes of their items (longest first), items follow class by class, and within a class
 // the sequence order.  dec_first[k] is the first decode item of class k.
-constexpr int kDecClasses = 4;
+constexpr int kDecClasses = 8;  // (4 measured 1% slower on the graph-captured decode)
 struct DecodeClasses {
   int dec_first[kDecClasses + 1];
   int split;  // the call's decode split size
@@ -219,7 +219,9 @@ __device__ __forceinline__ int dec_class(int max_kv, int split) {
   const int ns = max(1, ceil_div(max_kv, split));
   const long long len = even_split(max_kv, ns);  // keys per item
   const long long sp = split;
-  return 4 * len > 3 * sp ? 0 : 2 * len > sp ? 1 : 4 * len > sp ? 2 : 3;
+  // class k holds items of (K-1-k)/K .. (K-k)/K of the split, K = kDecClasses (0: longest)
+  const int q = (int)((len * kDecClasses - 1) / sp);
+  return kDecClasses - 1 - min(q, kDecClasses - 1);
 }
 
 // Item id -> (rank in a host-built order, index within the sequence); rank -1 past the last
@@ -1391,7 +1393,9 @@ __device__ GraphCall plan_graph_call(const GraphPlanArgs &p, PlanScratch &red) {
   c.split_pf = pf_units == 0 ? (1 << 30)
                : dec_units > 0 ? g_choose_split(pf_units, pf_long, 512, p.mixed_pf_items, p.max_splits)
                                : g_choose_split(pf_units, pf_long, 1024, p.prefill_only_items, p.max_splits);
-  long long n_cls[kDecClasses] = {0, 0, 0, 0}, n_pf = 0;
+  long long n_cls[kDecClasses], n_pf = 0;
+#pragma unroll
+  for (int kk = 0; kk < kDecClasses; ++kk) n_cls[kk] = 0;
   auto count_items = [&](int q_len, int kv) {
     const bool live = q_len > 0, dec = is_dec(q_len);
     const long long nd = (long long)p.Hkv * ceil_div(q_len * p.G, kDecodeRows) * max(1, ceil_div(kv, c.split_dec));
