@@ -581,3 +581,102 @@ def test_rotary_fp8_cache_stores_the_rotated_keys_codes():
     want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(kc[written], want)
     assert np.array_equal(kc[~written], b.k_cache[~written])
+
+
+# ------------------------------------------- KV-head-major layout, per-KV-head lengths ----
+# Over compacted per-KV-head tables every KV head of a sequence has its own length, hence its
+# own past (CompactAttention review, Figure 4: one table and one compacted length per KV head).
+
+_HM_Q = [1, 30, 5]
+_HM_KV = [[70, 33, 18], [40, 95, 30], [5, 22, 61]]   # [B][Hkv]: every head a different past
+
+
+def _head_major_batch(seed=41):
+    kv = np.array(_HM_KV)
+    pool = int(((kv + 15) // 16).sum()) + 5
+    return wl.ragged_batch("hm_pin", _HM_Q, kv, 6, 3, 32, 16, pool, seed, layout=wl.HEAD_MAJOR)
+
+
+def _head_sdpa(b, kc, vc, bi, g):
+    """fp64 causal SDPA of KV head g of sequence bi: its keys gathered by hand from its own
+    table row, the G query heads of the group, bottom-right mask at that head's own past."""
+    S, D = b.page_size, b.head_dim
+    G = b.num_q_heads // b.num_kv_heads
+    q0, q1 = int(b.cu_q_lens[bi]), int(b.cu_q_lens[bi + 1])
+    L = int(b.kv_lens[bi, g])
+    pos = np.arange(L)
+    pages = b.block_tables[bi, g, pos // S]
+    k = _f32(kc[pages, pos % S])                     # [L, D]
+    v = _f32(vc[pages, pos % S])
+    q = _f32(b.q[q0:q1, g * G:(g + 1) * G]).transpose(1, 0, 2)   # [G, q_len, D]
+    past = L - (q1 - q0)
+    mask = torch.arange(L)[None, :] <= (past + torch.arange(q1 - q0))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.copy())[None], torch.from_numpy(k[None, None].copy()).expand(1, G, L, D),
+        torch.from_numpy(v[None, None].copy()).expand(1, G, L, D), attn_mask=mask, scale=b.scale)
+    return ref[0].numpy().transpose(1, 0, 2)          # [q_len, G, D]
+
+
+def test_head_major_per_head_lengths_equal_per_head_sdpa():
+    """KV-head-major pages, kv_lens [B][Hkv] all different: after the fused write, each KV
+    head's rows equal fp64 SDPA over that head's own keys with its own bottom-right offset.
+    Catches: one head's length (or table row) used for every head, the write placing a head's
+    new keys at another head's past, a head mapping of h % Hkv instead of h / G."""
+    b = _head_major_batch()
+    kc, vc = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                             b.k_cache, b.v_cache, b.page_size, layout=wl.HEAD_MAJOR)
+    out = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
+                           b.page_size, b.num_kv_heads, layout=wl.HEAD_MAJOR)
+    G = b.num_q_heads // b.num_kv_heads
+    for bi in range(b.num_seqs):
+        q0, q1 = int(b.cu_q_lens[bi]), int(b.cu_q_lens[bi + 1])
+        for g in range(b.num_kv_heads):
+            ref = _head_sdpa(b, kc, vc, bi, g)
+            np.testing.assert_allclose(out[q0:q1, g * G:(g + 1) * G], ref, rtol=0, atol=1e-12)
+
+
+def test_head_major_write_places_each_head_at_its_own_past():
+    """The scatter with per-head lengths: token t of sequence b lands, for KV head g, at
+    position kv_len[b][g] - q_len + t of g's own table row (numpy fancy-index assignment);
+    every other byte is unchanged."""
+    b = _head_major_batch(seed=42)
+    kc, vc = oracle.write_kv(b.cu_q_lens, b.kv_lens, b.block_tables, b.k_new, b.v_new,
+                             b.k_cache, b.v_cache, b.page_size, layout=wl.HEAD_MAJOR)
+    ek, ev = b.k_cache.copy(), b.v_cache.copy()
+    S = b.page_size
+    for bi in range(b.num_seqs):
+        q0, q1 = int(b.cu_q_lens[bi]), int(b.cu_q_lens[bi + 1])
+        for g in range(b.num_kv_heads):
+            L = int(b.kv_lens[bi, g])
+            pos = np.arange(L - (q1 - q0), L)
+            pages = b.block_tables[bi, g, pos // S]
+            ek[pages, pos % S] = b.k_new[q0:q1, g]
+            ev[pages, pos % S] = b.v_new[q0:q1, g]
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+
+
+def test_head_major_relabelling_one_head_leaves_the_others():
+    """Moving KV head 1's pages of every sequence to fresh physical pages (and rewriting only
+    its table row) leaves every other head's rows bit-identical and head 1's too.  Catches: a
+    head reading another head's table row or pages."""
+    b = _head_major_batch(seed=43)
+    args = dict(layout=wl.HEAD_MAJOR)
+    base = oracle.attention(b.q, b.k_cache, b.v_cache, b.block_tables, b.cu_q_lens, b.kv_lens,
+                            b.scale, b.page_size, b.num_kv_heads, **args)
+    P = b.num_pages
+    kc = np.concatenate([b.k_cache, np.zeros_like(b.k_cache)])
+    vc = np.concatenate([b.v_cache, np.zeros_like(b.v_cache)])
+    tb = b.block_tables.copy()
+    rng = np.random.default_rng(5)
+    fresh = P + rng.permutation(P)
+    for bi in range(b.num_seqs):
+        row = tb[bi, 1]
+        used = row >= 0
+        new = fresh[row[used]]
+        kc[new], vc[new] = b.k_cache[row[used]], b.v_cache[row[used]]
+        kc[row[used]] = 0x7FC0                          # old pages poisoned with NaN
+        vc[row[used]] = 0x7FC0
+        tb[bi, 1, used] = new
+    out = oracle.attention(b.q, kc, vc, tb, b.cu_q_lens, b.kv_lens, b.scale, b.page_size,
+                           b.num_kv_heads, **args)
+    assert np.array_equal(out, base)
