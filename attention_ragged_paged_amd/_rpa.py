@@ -331,6 +331,8 @@ class PreparedAttention:
 
     For tight loops (benchmarks, serving steps) where the batch metadata does not change.
     The tensors passed here must stay alive and keep their shapes while the object is used.
+    Not for HIP graph capture: a call on a capturing stream raises RpaError
+    (RPA_ERR_UNSUPPORTED) and enqueues nothing; GraphAttention is the capturable form.
     """
 
     def __init__(self, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *,

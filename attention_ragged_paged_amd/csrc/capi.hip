@@ -209,6 +209,28 @@ rpa_status check_device() {
   return RPA_OK;
 }
 
+// rpa_attention fixes the split-merge tag and the plan in its kernel arguments on the host.
+// A captured call would replay with the same tag, find its counters already at the final
+// count and merge nothing, leaving split rows stale: such a call is refused (the device-
+// planned rpa_graph_attention exists for graphs).
+rpa_status refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the query's error is reported here, not by the next call
+    return fail(RPA_ERR_UNSUPPORTED,
+                "rpa_attention: the stream cannot be used while a graph is being captured "
+                "(hipStreamIsCapturing: %s); use rpa_graph_attention in graphs",
+                hipGetErrorString(e));
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(RPA_ERR_UNSUPPORTED,
+                "rpa_attention cannot be captured in a HIP graph (its plan and split-merge tag "
+                "are fixed on the host per call); use rpa_graph_attention, which plans on the "
+                "device");
+  return RPA_OK;
+}
+
 struct Plan {
   int kind = 0;         // RPA_KERNEL_DECODE / PREFILL / MIXED
   int dec_rows_max = 0;
@@ -499,6 +521,8 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
   st = check_device();
   if (st != RPA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = refuse_capture(hs);
+  if (st != RPA_OK) return st;
   const rpa::AttnKernel kind = static_cast<rpa::AttnKernel>(p.kind);
   const WorkspaceLayout wl = workspace_layout(shape, p);
   char *ws = static_cast<char *>(workspace);

@@ -185,6 +185,10 @@ int32_t rpa_select_kernel(const rpa_shape *shape);
  * accumulate, rounded to bf16 (round to nearest even); K and V are the cached
  * values (FP8: code values times the scales).  Sequences with
  * q_len == 0 are skipped; T == 0 returns RPA_OK without a launch.
+ * Not capturable: the kernel choice, split sizes and the split-merge tag are fixed on
+ * the host per call, so a replayed capture would merge nothing.  A call on a stream
+ * that is being captured into a HIP graph returns RPA_ERR_UNSUPPORTED and enqueues
+ * nothing; graphs use rpa_graph_attention.
  */
 rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
                          const int32_t *block_tables, const int32_t *cu_q_lens,

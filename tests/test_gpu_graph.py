@@ -148,3 +148,37 @@ def test_graph_invalid_batch_is_skipped_and_flagged():
     ga()
     _check(buf, b, "after invalid")
     assert ga.status() == 0
+
+
+def test_host_planned_call_refuses_capture():
+    """rpa_attention fixes its plan and split-merge tag on the host; under graph capture it
+    returns RPA_ERR_UNSUPPORTED and enqueues nothing, and it still runs eagerly afterwards."""
+    say("rpa_attention under capture is refused")
+    b = wl.ragged_batch("cap", [1, 1, 3], [900, 40, 300], HQ, HKV, D, S, POOL, 61)
+    d_q, d_kc, d_vc = bf16_dev(b.q), bf16_dev(b.k_cache), bf16_dev(b.v_cache)
+    d_kn, d_vn = bf16_dev(b.k_new), bf16_dev(b.v_new)
+    tb = torch.from_numpy(b.block_tables).cuda()
+    cu, kvl = torch.from_numpy(b.cu_q_lens).cuda(), torch.from_numpy(b.kv_lens).cuda()
+    side = torch.cuda.Stream()   # the call enqueues on the stream current at construction
+    with torch.cuda.stream(side):
+        attn = rpa.PreparedAttention(d_q, d_kc, d_vc, tb, cu, kvl, b.scale, k_new=d_kn,
+                                     v_new=d_vn, cu_q_lens_host=torch.from_numpy(b.cu_q_lens),
+                                     kv_lens_host=torch.from_numpy(b.kv_lens))
+    attn.out.fill_(3.0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    raised = None
+    with torch.cuda.graph(graph, stream=side):
+        try:
+            attn()
+        except rpa.RpaError as e:
+            raised = e
+    torch.cuda.synchronize()
+    assert raised is not None and raised.status == 2, raised
+    assert "rpa_graph_attention" in str(raised)
+    assert bool((attn.out.float() == 3.0).all()), "a refused call must enqueue nothing"
+    out = attn()
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_write(b)
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale, S, HKV)
+    compare(to_host_f32(out), ref, "eager call after a refused capture")
