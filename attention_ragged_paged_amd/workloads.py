@@ -283,12 +283,20 @@ def block_union_sparse(seed=5, context=131072, chunk=4096, density=0.1, column_s
     return batch
 
 
+def block_union_sparse_colshared(seed=5, **kw):
+    """block_union_sparse with the column-shared mask: one Bernoulli(0.1) draw per (head, KV
+    block) shared by all query blocks, so the union over Q-blocks stays sparse (about 34% of
+    the blocks per KV head after the union over the 4 heads of a group)."""
+    return block_union_sparse(seed=seed, column_shared=True, **kw)
+
+
 WORKLOADS = {
     "tiny_ragged": tiny_ragged,
     "llama3_decode": llama3_decode,
     "llama3_prefill": llama3_prefill,
     "mixed_chunked": mixed_chunked,
     "block_union_sparse": block_union_sparse,
+    "block_union_sparse_colshared": block_union_sparse_colshared,
     "llama3_decode_fp8": llama3_decode_fp8,
     "mixed_chunked_fp8": mixed_chunked_fp8,
 }

@@ -16,6 +16,9 @@ Workloads (all seeded synthetic inputs with Llama-3-8B attention shapes, 32/8 he
   llama3_prefill      4 x 2048 new tokens, no prior context, page 64
   mixed_chunked       one 512-token chunk at context 8192 + 96 decodes, page 16
   block_union_sparse  4096-query chunk at context 131072, KV-head-major page 64, 10% block mask
+  block_union_sparse_colshared
+                      the same chunk with a column-shared mask (one draw per head and KV block):
+                      attention over about a third of the context's pages per KV head
   tiny_ragged         the 3-sequence parity case (latency only)
   llama3_decode_fp8, mixed_chunked_fp8
                       the same batches over FP8 E4M3 K/V caches (1 byte an element, per-cache
@@ -25,6 +28,11 @@ Workloads (all seeded synthetic inputs with Llama-3-8B attention shapes, 32/8 he
 batches, TFLOP/s for the MFMA-bound prefill and sparse ones.  `roofline` rates the
 dominant kernel (the attention launch) against MI355X's published peaks: 8 TB/s HBM3E,
 2.5 PFLOP/s dense bf16 MFMA.  `cpu_baseline` times the CPU oracle on the host cores.
+
+The default run measures llama3_decode (the line's `value`) and then, under `workloads`, the
+MFMA-bound and mixed halves of the metric: llama3_prefill, mixed_chunked, block_union_sparse
+and block_union_sparse_colshared, each with its own throughput, roofline and CPU baseline
+(`--only` measures the named workload alone).
 """
 from __future__ import annotations
 
@@ -46,7 +54,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode HBM GB/s (% peak) + prefill/mixed TFLOP/s (% MFMA peak), tokens/s"
 WORKLOAD_BOUND = {"llama3_decode": "hbm", "mixed_chunked": "hbm", "tiny_ragged": "hbm",
                   "llama3_prefill": "mfma", "block_union_sparse": "mfma",
+                  "block_union_sparse_colshared": "mfma",
                   "llama3_decode_fp8": "hbm", "mixed_chunked_fp8": "hbm"}
+# measured after the headline workload in a default run
+EXTRA_WORKLOADS = ("llama3_prefill", "mixed_chunked", "block_union_sparse",
+                   "block_union_sparse_colshared")
 
 
 def log(msg):
@@ -115,6 +127,17 @@ def measured_traffic(workload):
 
 # ----------------------------------------------------------------- CPU baseline ----------
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(b, workload, bound, budget_s=12.0):
     """The oracle (unmodified) on the host cores over a bounded sample of the same batch."""
     import oracle
@@ -151,51 +174,23 @@ def cpu_baseline(b, workload, bound, budget_s=12.0):
     sample = (f"{len(idx)} of {rows_all} (token, head) rows (every {stride}th row) of the same "
               f"batch after the oracle's KV scatter, {reps} repetition(s), {dt:.2f} s each")
     return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": sample, "tokens_per_s": round(b.total_q * share / dt, 2)}
+            "sample": sample, "tokens_per_s": round(b.total_q * share / dt, 2),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 # ----------------------------------------------------------------- main --------------------
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_decode", choices=sorted(WORKLOAD_BOUND))
-    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
-                    help="how the caches are flushed before each step (none: warm caches)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 512 MiB device copy 3 times (reference for the "
-                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("host", "graph"), default="host",
-                    help="host: rpa_attention planned from host mirrors (the default); graph: "
-                         "rpa_graph_attention (device-side plan + persistent kernel) captured "
-                         "once in a HIP graph and replayed every step")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
-              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args, dev, with_cpu, cpu_budget):
+    """Time one workload: inputs in HBM, warmup steps, then args.steps timed steps (each with
+    the caches flushed first).  Returns the workload's record (throughput, roofline, CPU
+    baseline, configuration)."""
     import torch
     import attention_ragged_paged_amd as rpa
     from attention_ragged_paged_amd import workloads as wl
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    if args.calibrate_copy:
-        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 3}))
-        return
-    rpa.load_library()
-    bound = WORKLOAD_BOUND[args.workload]
-    log(f"[bench] building {args.workload} inputs")
-    b = wl.WORKLOADS[args.workload]()
+    bound = WORKLOAD_BOUND[name]
+    log(f"[bench] building {name} inputs")
+    b = wl.WORKLOADS[name]()
 
     def to_dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -214,7 +209,7 @@ def main():
     cu_h = torch.from_numpy(np.ascontiguousarray(b.cu_q_lens, np.int32))
     kvl_h = torch.from_numpy(np.ascontiguousarray(b.kv_lens, np.int32))
 
-    sparse = args.workload == "block_union_sparse"
+    sparse = "mask" in b.extra
     prep_steps = []
     if sparse:
         mask = torch.from_numpy(b.extra["mask"]).to(dev)
@@ -226,9 +221,11 @@ def main():
         att_kvl = u_kvl[None]
         att_kvl_h = u_kvl[None].cpu()
         b.extra["compacted_kv_lens"] = att_kvl_h.numpy()
-        import oracle as _o  # noqa: F401  (only for the CPU baseline below)
-        _, _, _, sel = _o.union_tables(b.extra["mask"], b.block_tables[0], past, ctx, b.page_size)
-        b.extra["allowed"] = sel[None]
+        if with_cpu:
+            import oracle as _o  # (only for the CPU baseline below)
+            _, _, _, sel = _o.union_tables(b.extra["mask"], b.block_tables[0], past, ctx,
+                                           b.page_size)
+            b.extra["allowed"] = sel[None]
         b.extra["union_density"] = (u_counts.cpu().numpy() / (ctx // b.page_size)).round(4).tolist()
 
         def build_tables():
@@ -277,14 +274,14 @@ def main():
         if ev:
             ev[2].record()
 
-    log(f"[bench] kernel kind {kind}; warmup {args.warmup}")
+    log(f"[bench] {name}: kernel kind {kind}; warmup {args.warmup}")
     for _ in range(args.warmup):
         flush()
         one_step()
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] {name}: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -294,9 +291,11 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
     attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     ms = float(step_ms.mean())
     attn_avg_ms = float(attn_ms.mean())
 
+    flops = causal_flops(b, b.extra.get("compacted_kv_lens"))
     if bound == "hbm":
         work = step_bytes(b)
         value = work / (ms * 1e-3) / 1e9
@@ -305,46 +304,111 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     else:
-        work = causal_flops(b, b.extra.get("compacted_kv_lens"))
+        work = flops
         value = work / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
         ach = work / (attn_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload) if args.path == "host" else None
+    roof["traffic"] = measured_traffic(name) if args.path == "host" else None
     roof["kernel"] = {1: "decode_kernel", 2: "prefill_kernel", 3: "mixed_kernel"}[kind] + \
         " (one launch: KV write, attention, split merge)"
     if args.path == "graph":
         roof["kernel"] = "graph replay: graph_kernel (device-planned, persistent)"
     roof["avg_launch_ms"] = round(attn_avg_ms, 5)
+    # the metric's MFMA half for every workload: flops of the attention launch
+    mfma = {"tflops": round(flops / (attn_avg_ms * 1e-3) / 1e12, 2),
+            "frac_of_mfma_peak": round(flops / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_step": flops}
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(b, args.workload, bound)
+    if with_cpu:
+        log(f"[bench] {name}: timing the CPU oracle")
+        cpu = cpu_baseline(b, name, bound, budget_s=cpu_budget)
 
-    cfg = {"workload": args.workload, "num_seqs": b.num_seqs, "total_q": b.total_q,
+    cfg = {"workload": name, "num_seqs": b.num_seqs, "total_q": b.total_q,
            "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
            "page_size": b.page_size, "pool_pages": b.num_pages, "layout":
            "seq_major" if b.layout == 0 else "kv_head_major", "seed": b.seed,
            "sum_kv_len": int(b.kv_lens.reshape(b.num_seqs, -1)[:, 0].sum()),
            "cache_flush": args.flush, "parallelism": "none (one GPU)", "path": args.path}
-    if sparse:
-        cfg["union_density"] = b.extra["union_density"]
-    line = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+    rec = {
+        "value": round(value, 3), "unit": unit, "ms_per_step": round(ms, 5),
         "dtype": "bf16 (q, out, new K/V), fp8-e4m3 K/V cache" if b.kv_fp8 else "bf16",
-        "data": ("synthetic (seeded N(0,1) bf16 values, FP8 cache codes drawn per field, "
-                 "Llama-3-8B attention shapes)" if b.kv_fp8 else
-                 "synthetic (seeded N(0,1) bf16 values, Llama-3-8B attention shapes)"),
         "config": cfg,
         "tokens_per_s": round(b.total_q / (ms * 1e-3), 1),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 5) for p in (10, 50, 90)],
         "work_per_step": work, "wall_s_timed_loop": round(wall, 4),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "mfma": mfma, "cpu_baseline": cpu,
     }
+    if sparse:
+        cfg["union_density"] = b.extra["union_density"]
+        cfg["compacted_kv_lens"] = [int(x) for x in b.extra["compacted_kv_lens"].reshape(-1)]
+        cfg["mask"] = "column_shared" if name.endswith("colshared") else "per (head, Q-block)"
+        rec["union_build_ms"] = round(float(prep_ms.mean()), 5)
+    del attn, q, kn, vn, kc, vc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_decode", choices=sorted(WORKLOAD_BOUND))
+    ap.add_argument("--only", action="store_true",
+                    help="measure the named workload alone (no extra workloads)")
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                    help="how the caches are flushed before each step (none: warm caches)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("host", "graph"), default="host",
+                    help="host: rpa_attention planned from host mirrors (the default); graph: "
+                         "rpa_graph_attention (device-side plan + persistent kernel) captured "
+                         "once in a HIP graph and replayed every step")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_ragged_paged_amd as rpa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 3}))
+        return
+    rpa.load_library()
+    with_cpu = not args.no_cpu_baseline
+    head = measure(args.workload, args, dev, with_cpu, 12.0)
+    extras = {}
+    if not args.only and args.workload == "llama3_decode":
+        for name in EXTRA_WORKLOADS:
+            extras[name] = measure(name, args, dev, with_cpu, 8.0)
+
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": ("synthetic (seeded N(0,1) bf16 values, FP8 cache codes drawn per field, "
+                 "Llama-3-8B attention shapes)" if "fp8" in head["dtype"] else
+                 "synthetic (seeded N(0,1) bf16 values, Llama-3-8B attention shapes)"),
+    }
+    line.update({k: v for k, v in head.items() if k not in ("value", "unit", "ms_per_step", "dtype")})
+    if extras:
+        line["workloads"] = extras
     print(json.dumps(line), flush=True)
 
 
