@@ -6,6 +6,7 @@ CPU fallback: every call fails loudly if the library or a gfx950 device is missi
 
     write_kv(k_new, v_new, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, ...)
     attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, ...)
+    attention_noalloc(...)   # the same without a workspace (static device scratch)
     build_union_tables(mask, base_tables, past, kv_len, page_size)
     rotary_write_kv(q, k, v, k_cache, v_cache, ...)   # rotary + packed-QKV split + scatter
     GraphAttention(...)   # device-planned call that a HIP graph can capture
@@ -26,7 +27,9 @@ from ._rpa import (  # noqa: F401
     PreparedAttention,
     PreparedWriteKV,
     RpaError,
+    NOALLOC_SCRATCH_BYTES,
     attention,
+    attention_noalloc,
     build_union_tables,
     kv_dtype_of,
     library_path,

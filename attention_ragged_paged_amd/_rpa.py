@@ -27,6 +27,7 @@ _STATUS = {0: "RPA_OK", 1: "RPA_ERR_INVALID_ARGUMENT", 2: "RPA_ERR_UNSUPPORTED",
            3: "RPA_ERR_WORKSPACE_TOO_SMALL", 4: "RPA_ERR_HIP"}
 
 EXPORTED = ("rpa_write_kv", "rpa_attention_workspace_size", "rpa_select_kernel", "rpa_attention",
+            "rpa_attention_noalloc",
             "rpa_graph_workspace_size", "rpa_graph_attention", "rpa_build_union_tables",
             "rpa_rotary_write_kv", "rpa_last_error")
 
@@ -92,6 +93,9 @@ def load_library():
     lib.rpa_select_kernel.restype = i32
     lib.rpa_attention.argtypes = [shp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.rpa_attention.restype = ctypes.c_int
+    lib.rpa_attention_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                          vp, vp]
+    lib.rpa_attention_noalloc.restype = ctypes.c_int
     gshp = ctypes.POINTER(RpaGraphShape)
     lib.rpa_graph_workspace_size.argtypes = [gshp]
     lib.rpa_graph_workspace_size.restype = sz
@@ -299,6 +303,28 @@ def attention(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *, k
                              _ptr(cu_q_lens), _ptr(kv_lens), float(scale), _ptr(k_new),
                              _ptr(v_new), _ptr(out), _ptr(workspace), ws_bytes,
                              _stream(q.device)))
+    return out
+
+
+# Bytes of the library's static scratch (RPA_NOALLOC_SCRATCH_BYTES in include/rpa.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attention_noalloc(q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale, *, out,
+                      k_new=None, v_new=None, cu_q_lens_host=None, kv_lens_host=None,
+                      kernel=KERNEL_AUTO, k_scale=1.0, v_scale=1.0):
+    """rpa_attention_noalloc: attention whose split partials live in the library's static
+    device scratch (no workspace); writes into the caller's ``out`` and returns it.  Calls
+    that overlap in time on one GPU race on that scratch."""
+    lib = load_library()
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 cu_q_lens=cu_q_lens, kv_lens=kv_lens, k_new=k_new, v_new=v_new, out=out)
+    shape = _shape_for(q.shape[1], k_cache, block_tables, cu_q_lens, kv_lens, cu_q_lens_host,
+                       kv_lens_host, kernel, k_scale, v_scale, v_cache)
+    _check(lib.rpa_attention_noalloc(shape.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_tables), _ptr(cu_q_lens), _ptr(kv_lens),
+                                     float(scale), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                     _stream(q.device)))
     return out
 
 

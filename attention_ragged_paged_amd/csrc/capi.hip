@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/rpa.h"
@@ -499,30 +500,35 @@ int32_t rpa_select_kernel(const rpa_shape *shape) {
   return make_plan(shape).kind;
 }
 
-rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
-                         const int32_t *block_tables, const int32_t *cu_q_lens,
-                         const int32_t *kv_lens, float scale, const void *k_new,
-                         const void *v_new, void *out, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the attention entry points; on success *p is the call's plan.
+rpa_status check_attention_call(const rpa_shape *shape, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                const int32_t *cu_q_lens, const int32_t *kv_lens, float scale,
+                                const void *k_new, const void *v_new, const void *out,
+                                const char *name, Plan *p) {
   rpa_status st = validate(shape, true);
   if (st != RPA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f))
     return fail(RPA_ERR_INVALID_ARGUMENT, "scale %g must be finite and > 0", (double)scale);
-  if (shape->total_q == 0) return ok();
+  if (shape->total_q == 0) return RPA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !cu_q_lens || !kv_lens || !out)
-    return fail(RPA_ERR_INVALID_ARGUMENT, "rpa_attention: a device pointer is NULL");
+    return fail(RPA_ERR_INVALID_ARGUMENT, "%s: a device pointer is NULL", name);
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(RPA_ERR_INVALID_ARGUMENT, "k_new and v_new must both be given or both be NULL");
-  const Plan p = make_plan(shape);
+  *p = make_plan(shape);
+  return RPA_OK;
+}
+
+// The launch of a checked call with its plan, over a workspace of the plan's size.
+rpa_status launch_planned(const rpa_shape *shape, const Plan &p, const void *q, void *k_cache,
+                          void *v_cache, const int32_t *block_tables, const int32_t *cu_q_lens,
+                          const int32_t *kv_lens, float scale, const void *k_new,
+                          const void *v_new, void *out, void *workspace, hipStream_t hs) {
   const size_t need = workspace_bytes_for(shape, p);
-  if (workspace_bytes < need || (need > 0 && !workspace))
-    return fail(RPA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
-                workspace_bytes, need);
-  st = check_device();
-  if (st != RPA_OK) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = refuse_capture(hs);
-  if (st != RPA_OK) return st;
   const rpa::AttnKernel kind = static_cast<rpa::AttnKernel>(p.kind);
   const WorkspaceLayout wl = workspace_layout(shape, p);
   char *ws = static_cast<char *>(workspace);
@@ -626,6 +632,94 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
                                        p.n_pf_items + p.n_dec_items, hs);
   if (e != hipSuccess) return fail(RPA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// ------------------------------------------------------------ static scratch ----
+//
+// rpa_attention_noalloc keeps the split partials and arrival counters in this file-scope
+// array instead of a caller's workspace.  In host code `scratch` is only a stand-in for the
+// symbol: its device address, one per GPU (each GPU holds its own copy of the array), comes
+// from hipGetSymbolAddress with that device current and is the only form ever passed on.
+// Nothing in it needs clearing: the counters carry each call's tag, so whatever an earlier
+// call left reads as zero.
+constexpr size_t kScratchBytes = RPA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+rpa_status scratch_of_current_device(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RPA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RPA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(RPA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, void *v_cache,
+                         const int32_t *block_tables, const int32_t *cu_q_lens,
+                         const int32_t *kv_lens, float scale, const void *k_new,
+                         const void *v_new, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  Plan p;
+  rpa_status st = check_attention_call(shape, q, k_cache, v_cache, block_tables, cu_q_lens,
+                                       kv_lens, scale, k_new, v_new, out, "rpa_attention", &p);
+  if (st != RPA_OK) return st;
+  if (shape->total_q == 0) return ok();
+  const size_t need = workspace_bytes_for(shape, p);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(RPA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
+                workspace_bytes, need);
+  st = check_device();
+  if (st != RPA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = refuse_capture(hs);
+  if (st != RPA_OK) return st;
+  return launch_planned(shape, p, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale,
+                        k_new, v_new, out, workspace, hs);
+}
+
+rpa_status rpa_attention_noalloc(const rpa_shape *shape, const void *q, void *k_cache,
+                                 void *v_cache, const int32_t *block_tables,
+                                 const int32_t *cu_q_lens, const int32_t *kv_lens, float scale,
+                                 const void *k_new, const void *v_new, void *out, void *stream) {
+  Plan p;
+  rpa_status st = check_attention_call(shape, q, k_cache, v_cache, block_tables, cu_q_lens,
+                                       kv_lens, scale, k_new, v_new, out,
+                                       "rpa_attention_noalloc", &p);
+  if (st != RPA_OK) return st;
+  if (shape->total_q == 0) return ok();
+  const size_t need = workspace_bytes_for(shape, p);
+  if (need > kScratchBytes)
+    return fail(RPA_ERR_WORKSPACE_TOO_SMALL,
+                "rpa_attention_noalloc: this batch needs %zu bytes of split partials, more than "
+                "the library's static scratch of %zu bytes; call rpa_attention with a workspace",
+                need, kScratchBytes);
+  st = check_device();
+  if (st != RPA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = refuse_capture(hs);
+  if (st != RPA_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != RPA_OK) return st;
+  return launch_planned(shape, p, q, k_cache, v_cache, block_tables, cu_q_lens, kv_lens, scale,
+                        k_new, v_new, out, need > 0 ? ws : nullptr, hs);
 }
 
 // ----------------------------------------------------------------- graph-capturable ----

@@ -197,6 +197,29 @@ rpa_status rpa_attention(const rpa_shape *shape, const void *q, void *k_cache, v
                          void *stream);
 
 /*
+ * rpa_attention_noalloc -- rpa_attention for callers that cannot allocate device memory
+ * at all (code that must not call hipMalloc: under HIP graph capture set-up, in tight
+ * serving loops, in harnesses that forbid it), not even a workspace once.
+ *   Arguments, results and errors as rpa_attention, without the workspace: the split
+ *   partials and arrival counters live in a static device array of
+ *   RPA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ *   process ends (its address is looked up once per device, on the first call there).
+ *   A batch whose partials need more (rpa_attention_workspace_size(shape) bytes) returns
+ *   RPA_ERR_WORKSPACE_TOO_SMALL without a launch.  The call allocates nothing and needs
+ *   nothing cleared: counters carry a per-call tag, so what an earlier call left behind
+ *   reads as stale.  Every call on one GPU shares that GPU's array, so calls that overlap
+ *   in time on one GPU (different streams, threads or processes' contexts) race and give
+ *   wrong results; calls ordered on one stream are safe.  Kernels and plan are those of
+ *   rpa_attention, so the output is bit-identical to it.  Not capturable (as
+ *   rpa_attention).
+ */
+#define RPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rpa_status rpa_attention_noalloc(const rpa_shape *shape, const void *q, void *k_cache,
+                                 void *v_cache, const int32_t *block_tables,
+                                 const int32_t *cu_q_lens, const int32_t *kv_lens, float scale,
+                                 const void *k_new, const void *v_new, void *out, void *stream);
+
+/*
  * Graph-capturable attention: the same computation as rpa_attention, planned on the
  * device.  rpa_attention reads the batch's lengths on the host to choose the kernel, the
  * KV split sizes and the grid; that ties every call to host data and keeps it out of a
