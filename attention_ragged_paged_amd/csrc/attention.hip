@@ -350,7 +350,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   };
   auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
-    const int page = __builtin_amdgcn_readlane(pg_lane, i);
+    const int page = read_page(__builtin_amdgcn_readlane(pg_lane, i));
     if constexpr (KV8) {
       // register t: the row's 16 codes, or for a new key the first 8 of its bf16 values (the
       // other 8 are loaded when the chunk is staged); every lane loads, so the waits before
@@ -389,7 +389,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   };
   auto process_chunk = [&](int base, int i, const u32x4 *kr, const u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
-    const int page = __builtin_amdgcn_readlane(pg_lane, i);
+    const int page = __builtin_amdgcn_readlane(pg_lane, i);  // negative: a bad entry, no store
     // Stage in LDS (V rows of keys past the item's range are zeroed: they may hold anything);
     // the writer item also stores the new keys into their page slots.
     if constexpr (KV8) {
@@ -405,7 +405,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
           const u32x4 vhi = *reinterpret_cast<const u32x4 *>(a.v_new + new_off(key) + 8);
           kc = quantize16(kr[t], khi, a.k_inv);
           vc = quantize16(vr[t], vhi, a.v_inv);
-          if (writer && key < k_end) {
+          if (writer && key < k_end && page >= 0) {
             const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 16 * lchk;
             *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(k8) + coff) = kc;
             *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(v8) + coff) = vc;
@@ -427,7 +427,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
       const int key = key0 + r;
       *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, lchk)) = kr[t];
       *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, lchk)) = key < k_end ? vr[t] : u32x4{0u, 0u, 0u, 0u};
-      if (writer && key >= past && key < k_end) {
+      if (writer && key >= past && key < k_end && page >= 0) {
         const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 8 * lchk;
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + coff) = kr[t];
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + coff) = vr[t];
@@ -483,7 +483,9 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
 
   for (int base = 0; base < n_w; base += 64) {
     const int n = min(64, n_w - base);
-    pg_lane = lane < n ? table_at(a, b, g, (k_begin + 16 * (w + 4 * (base + lane))) >> a.page_shift) : 0;
+    pg_lane = lane < n ? checked_page(table_at(a, b, g, (k_begin + 16 * (w + 4 * (base + lane))) >> a.page_shift),
+                                      a.num_pages)
+                       : 0;
     if constexpr (KV8) {
       // An FP8 chunk is half the bytes of a bf16 one: four chunks stay in flight (a register
       // ring) so that a wave keeps as many bytes in flight as the bf16 loop does.
@@ -653,8 +655,17 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   ItemRef it;
   int b, q0, q_len, max_kv;
   if (order != nullptr && order->n > 0) {  // everything from the kernel arguments
-    it = ordered_item(*order, id);
-    if (it.b < 0) return;
+    if (order->interleave) {
+      // rank r of every sequence before rank r + 1 of any: id = (r n + i) Hkv nsplit + rest
+      if (id >= order->first[order->n]) return;
+      const int per_rank = a.Hkv * max(1, ceil_div(order->kv[0], a.split_pf));
+      const int r = id / (order->n * per_rank);
+      const int i = (id / per_rank) % order->n;
+      it = {i, r * per_rank + id % per_rank};
+    } else {
+      it = ordered_item(*order, id);
+      if (it.b < 0) return;
+    }
     b = order->seq[it.b];
     q0 = order->q0[it.b];
     q_len = order->q_len[it.b];
@@ -721,7 +732,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   int pg_lane = 0, pg_blk0 = 0;
   auto fetch_pages = [&](int blk0) {
     const int blk = blk0 + lane;
-    pg_lane = blk < blk_end ? table_at(a, b, g, blk) : 0;
+    pg_lane = blk < blk_end ? checked_page(table_at(a, b, g, blk), a.num_pages) : 0;
     pg_blk0 = blk0;
     // Wait here, once per window: otherwise every page lookup would wait for all loads in
     // flight, the tile loads included.
@@ -753,7 +764,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(a.k_new + nb) + lo), kdst);
       load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(a.v_new + nb) + lo), vdst);
     } else {
-      const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+      const int page = read_page(__builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0));
       const int64_t cb = (int64_t)page * pstride + (g0 & page_mask) * sstride;
       load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(kc_g + cb) + lo), kdst);
       load_lds16(reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(vc_g + cb) + lo), vdst);
@@ -790,7 +801,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
         const int pos = g0 + lr;
         const int64_t off = pos >= past
                                 ? new_row0 + (int64_t)pos * new_stride + ld_c8
-                                : (int64_t)__builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0) *
+                                : (int64_t)read_page(__builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0)) *
                                           pstride + (pos & page_mask) * sstride + ld_c8;
         load_lds16((pos >= past ? a.k_new : kc_g) + off, kdst);
         load_lds16((pos >= past ? a.v_new : vc_g) + off, vdst);
@@ -814,7 +825,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       const int c = cid % kChunks;
       const int pos = kt0 + key;
       const int page = __shfl(pg_lane, (pos >> a.page_shift) - pg_blk0);  // every lane takes part
-      if (pos >= past && pos < k_end) {
+      if (pos >= past && pos < k_end && page >= 0) {
         const int64_t off = kv_row_offset(a, page, pos & page_mask, g) + c * 8;
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + off) =
             *reinterpret_cast<const u32x4 *>(kbuf[buf] + lds_off<D>(key, c));
@@ -846,7 +857,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       const int key = min(g0 + lr8, k_end - 1);                  // the range's last key
       // Every lane loads twice, from addresses chosen per lane (no branch): a cached row's 16
       // codes (the second load repeats the first, a cache hit), or a new row's 16 bf16 values.
-      const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+      const int page = read_page(__builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0));
       const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
       const int64_t noff = new_row0 + (int64_t)key * new_stride + 16 * c16;
       const bool is_new = fused && key >= past;
@@ -871,8 +882,8 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       if (fused && key >= past) {
         kc = quantize16(kst[2 * u], kst[2 * u + 1], a.k_inv);
         vc = quantize16(vst[2 * u], vst[2 * u + 1], a.v_inv);
-        if (writer && kt0 + row < k_end) {  // the item owning the last query rows stores them
-          const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+        const int page = __builtin_amdgcn_readlane(pg_lane, (g0 >> a.page_shift) - pg_blk0);
+        if (writer && kt0 + row < k_end && page >= 0) {  // the item owning the last query rows stores them
           const int64_t off = (int64_t)page * pstride + (key & page_mask) * sstride + 16 * c16;
           *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(kc8) + off) = kc;
           *reinterpret_cast<u32x4 *>(const_cast<uint8_t *>(vc8) + off) = vc;

@@ -384,6 +384,7 @@ rpa_status write_kv_impl(const rpa_shape *s, const void *k_new, const void *v_ne
   w.T = s->total_q;
   w.Hkv = s->num_kv_heads;
   w.page_shift = ilog2(s->page_size);
+  w.num_pages = s->num_pages;
   fill_layout(s, w.page_stride, w.slot_stride, w.head_stride, w.bt_seq_stride, w.bt_head_stride,
               w.kvl_seq_stride, w.kvl_head_stride);
   fill_kv_dtype(w, s->kv_dtype, s->k_scale, s->v_scale);
@@ -481,6 +482,7 @@ rpa_status rpa_rotary_write_kv(const rpa_shape *shape, const void *q, const void
   r.rotary_dim = rd;
   r.interleaved = rd > 0 && rotary->interleaved ? 1 : 0;
   r.page_shift = ilog2(shape->page_size);
+  r.num_pages = shape->num_pages;
   fill_layout(shape, r.page_stride, r.slot_stride, r.head_stride, r.bt_seq_stride,
               r.bt_head_stride, r.kvl_seq_stride, r.kvl_head_stride);
   fill_kv_dtype(r, shape->kv_dtype, shape->k_scale, shape->v_scale);
@@ -552,6 +554,7 @@ rpa_status launch_planned(const rpa_shape *shape, const Plan &p, const void *q, 
   a.Hkv = shape->num_kv_heads;
   a.G = shape->num_q_heads / shape->num_kv_heads;
   a.page_shift = ilog2(shape->page_size);
+  a.num_pages = shape->num_pages;
   fill_layout(shape, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride,
               a.bt_head_stride, a.kvl_seq_stride, a.kvl_head_stride);
   fill_kv_dtype(a, shape->kv_dtype, shape->k_scale, shape->v_scale);
@@ -569,6 +572,7 @@ rpa_status launch_planned(const rpa_shape *shape, const Plan &p, const void *q, 
   // its items load no lengths before their query and table loads.
   rpa::SeqOrder order;
   order.n = 0;
+  order.interleave = 0;
   if (kind == rpa::AttnKernel::kPrefill) {
     const int G = a.G;
     int n = 0, first = 0;
@@ -590,6 +594,10 @@ rpa_status launch_planned(const rpa_shape *shape, const Plan &p, const void *q, 
     }
     order.first[n] = first;
     order.n = n;
+    bool same = n > 1;
+    for (int i = 1; i < n && same; ++i)
+      same = order.q_len[i] == order.q_len[0] && order.kv[i] == order.kv[0];
+    order.interleave = same ? 1 : 0;
   } else if (p.n_dec_items > 0) {
     const int G = a.G;
     int idx[rpa::kMaxOrderedSeqs];
@@ -855,6 +863,7 @@ rpa_status rpa_graph_attention(const rpa_graph_shape *shape, const void *q, void
   a.Hkv = shape->num_kv_heads;
   a.G = shape->num_q_heads / shape->num_kv_heads;
   a.page_shift = ilog2(shape->page_size);
+  a.num_pages = shape->num_pages;
   fill_layout(&s, a.page_stride, a.slot_stride, a.head_stride, a.bt_seq_stride, a.bt_head_stride,
               a.kvl_seq_stride, a.kvl_head_stride);
   fill_kv_dtype(a, shape->kv_dtype, shape->k_scale, shape->v_scale);

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(256) void rotary_write_kernel(RotaryArgs r) {
   const u32x4 kv = rotated(r.k + (int64_t)token * r.kv_stride + (int64_t)g * D);
   const u32x4 vv = *reinterpret_cast<const u32x4 *>(r.v + (int64_t)token * r.kv_stride + (int64_t)g * D + d0);
   const int page = r.tables[b * r.bt_seq_stride + g * r.bt_head_stride + (pos >> r.page_shift)];
+  if ((unsigned)page >= (unsigned)r.num_pages) return;  // a bad table entry is never stored through
   const int slot = pos & ((1 << r.page_shift) - 1);
   const int64_t dst = (int64_t)page * r.page_stride + (int64_t)slot * r.slot_stride +
                       (int64_t)g * r.head_stride + d0;

@@ -55,6 +55,7 @@ struct AttnArgs {
   unsigned long long call_tag;   // this call's tag in bits 24..63 (count in bits 0..23)
   int32_t B, T, Hq, Hkv, G;
   int32_t page_shift;       // log2(page size)
+  int32_t num_pages;        // pages in each cache: table entries outside [0, num_pages) are bad
   int64_t page_stride, slot_stride, head_stride;  // cache element strides
   int32_t bt_seq_stride, bt_head_stride;          // table entry (b, g, i) = tables[b*seq + g*head + i]
   int32_t kvl_seq_stride, kvl_head_stride;        // kv_len(b, g) = kv_lens[b*seq + g*head]
@@ -71,6 +72,16 @@ struct AttnArgs {
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Block-table entries are preconditions, not checked on the host: an entry outside
+// [0, num_pages) is kept in a page window as page 0 with the sign bit set, so that readers
+// stay inside the cache (the keys they read there are unspecified) and writers, which test
+// the sign bit, never store through it.
+constexpr int kBadPage = (int)0x80000000u;
+__device__ __forceinline__ int checked_page(int entry, int num_pages) {
+  return (unsigned)entry < (unsigned)num_pages ? entry : kBadPage;
+}
+__device__ __forceinline__ int read_page(int checked) { return checked & 0x7fffffff; }
 
 // The thread index, read once per work item behind an empty asm: values derived from it are
 // then computed per item instead of being hoisted out of a persistent kernel's item loop,

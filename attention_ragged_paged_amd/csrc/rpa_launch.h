@@ -18,6 +18,7 @@ struct WriteArgs {
   const int32_t *kv_lens;
   int32_t B, T, Hkv;
   int32_t page_shift;
+  int32_t num_pages;         // a table entry outside [0, num_pages) is never stored through
   int64_t page_stride, slot_stride, head_stride;
   int32_t bt_seq_stride, bt_head_stride;
   int32_t kvl_seq_stride, kvl_head_stride;
@@ -35,6 +36,7 @@ struct RotaryArgs {
   int32_t B, T, Hq, Hkv;
   int32_t rotary_dim, interleaved;  // rotary_dim: 0 or a multiple of 16, <= D
   int32_t page_shift;
+  int32_t num_pages;                // a table entry outside [0, num_pages) is never stored through
   int64_t page_stride, slot_stride, head_stride;
   int32_t bt_seq_stride, bt_head_stride;
   int32_t kvl_seq_stride, kvl_head_stride;
@@ -60,6 +62,10 @@ hipError_t launch_write_kv(const WriteArgs &a, int D, hipStream_t stream);
 constexpr int kMaxOrderedSeqs = 160;  // keeps the kernel arguments under 4 KB
 struct SeqOrder {
   int32_t n;
+  // prefill launch whose listed sequences all have the same q_len and kv_len: items run q-tile
+  // rank by rank across the sequences (every sequence's heaviest tiles first), not sequence
+  // by sequence, so that the launch ends on the lightest items of every sequence
+  int32_t interleave;
   int32_t first[kMaxOrderedSeqs + 1];  // first[n] = number of items
   int32_t seq[kMaxOrderedSeqs];
   int32_t q0[kMaxOrderedSeqs];         // cu_q_lens[seq]

@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   const int kv_len = a.kv_lens[b * a.kvl_seq_stride + g * a.kvl_head_stride];
   const int pos = kv_len - q_len + (token - q0);
   const int page = a.tables[b * a.bt_seq_stride + g * a.bt_head_stride + (pos >> a.page_shift)];
+  if ((unsigned)page >= (unsigned)a.num_pages) return;  // a bad table entry is never stored through
   const int slot = pos & ((1 << a.page_shift) - 1);
   const int64_t dst = (int64_t)page * a.page_stride + (int64_t)slot * a.slot_stride +
                       (int64_t)g * a.head_stride + c * 8;

@@ -31,9 +31,12 @@
  *     null stream).  Host arrays are read only during the call.
  *   - No call aborts or throws.  A non-zero status comes with a message from
  *     rpa_last_error() (thread-local).  Device contents are preconditions that
- *     are NOT checked: block-table entries of every block a sequence uses must
- *     lie in [0, num_pages), and slots written for different sequences must be
- *     disjoint.
+ *     are NOT checked on the host: block-table entries of every block a sequence
+ *     uses must lie in [0, num_pages), and slots written for different sequences
+ *     must be disjoint.  The kernels never store through an entry outside
+ *     [0, num_pages) (the new K/V of such a block are dropped) and never read
+ *     outside the caches through one (the keys read for it are unspecified, so
+ *     the rows that see them are); entries past a sequence's blocks are not read.
  */
 #ifndef RPA_H
 #define RPA_H

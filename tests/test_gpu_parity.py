@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 KERNELS = [rpa.KERNEL_AUTO, rpa.KERNEL_DECODE, rpa.KERNEL_PREFILL, rpa.KERNEL_MIXED]
 
 
-def _full_check(b, kernel=rpa.KERNEL_AUTO, fused=True, label=""):
+def _full_check(b, kernel=rpa.KERNEL_AUTO, fused=True, label="", typical=None):
     d = Dev(b)
     if not fused:
         d.write()
@@ -31,7 +31,7 @@ def _full_check(b, kernel=rpa.KERNEL_AUTO, fused=True, label=""):
     assert np.array_equal(to_host_bits(d.v_cache), vc), f"{label}: V cache differs"
     ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
                            b.page_size, b.num_kv_heads, layout=b.layout)
-    return compare(to_host_f32(out), ref, label)
+    return compare(to_host_f32(out), ref, label, typical=typical)
 
 
 # ------------------------------------------------------------------------------ write ----
@@ -118,12 +118,12 @@ def test_long_decode_sequence_many_chunks():
     ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale, 16, 1,
                            rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
-    compare(got, ref, "long decode")
+    compare(got, ref, "long decode", typical=(1e-3, 1e-4))
 
 
 # --------------------------------------------------------------- full-size workloads ----
 
-def _sampled(b, n_rows, label, kernel=rpa.KERNEL_AUTO, check_cache=True):
+def _sampled(b, n_rows, label, kernel=rpa.KERNEL_AUTO, check_cache=True, typical=None):
     d = Dev(b)
     out = d.attention(kernel=kernel)
     kc, vc = oracle_after_write(b)
@@ -134,17 +134,17 @@ def _sampled(b, n_rows, label, kernel=rpa.KERNEL_AUTO, check_cache=True):
     ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
                            b.page_size, b.num_kv_heads, layout=b.layout, rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
-    return compare(got, ref, label)
+    return compare(got, ref, label, typical=typical)
 
 
 def test_llama3_decode_full_size():
     say("llama3_decode full size (64 seqs, kv U[512,4096], 20k-page pool)")
-    _sampled(wl.llama3_decode(), 512, "llama3 decode")
+    _sampled(wl.llama3_decode(), 512, "llama3 decode", typical=(3e-3, 3e-4))
 
 
 def test_llama3_prefill_full_size():
     say("llama3_prefill full size (4 x 2048, page 64)")
-    _sampled(wl.llama3_prefill(), 256, "llama3 prefill")
+    _sampled(wl.llama3_prefill(), 256, "llama3 prefill", typical=(1e-2, 5e-4))
 
 
 def test_mixed_chunked_full_size():
@@ -153,7 +153,7 @@ def test_mixed_chunked_full_size():
     d = Dev(b)
     assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_MIXED
     del d
-    _sampled(b, 400, "mixed chunked")
+    _sampled(b, 400, "mixed chunked", typical=(2e-3, 2e-4))
 
 
 # ------------------------------------------------------------------ union tables -------
@@ -208,7 +208,7 @@ def test_block_union_sparse_full_size(column_shared, fused):
                            b.page_size, b.num_kv_heads, layout=wl.HEAD_MAJOR,
                            block_allowed=sel[None], rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
-    compare(got, ref, f"sparse column_shared={column_shared} fused={fused}")
+    compare(got, ref, f"sparse column_shared={column_shared} fused={fused}", typical=(5e-4, 6e-5))
 
 
 # --------------------------------------------------------------- layouts and extremes ----
@@ -248,7 +248,7 @@ def test_long_context_prefill_splits():
     d = Dev(b)
     assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_PREFILL
     del d
-    _sampled(b, 160, "long-context prefill")
+    _sampled(b, 160, "long-context prefill", typical=(1.5e-3, 1.2e-4))
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(24, 8, 64), (16, 2, 64), (8, 8, 128), (12, 4, 128)])
@@ -262,14 +262,14 @@ def test_prefill_split_rows_every_group_size(Hq, Hkv, D):
     d = Dev(b)
     assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_PREFILL
     del d
-    _full_check(b, label=f"prefill split rows {Hq}/{Hkv}/{D}")
+    _full_check(b, label=f"prefill split rows {Hq}/{Hkv}/{D}", typical=(2e-3, 2e-4))
 
 
 def test_long_context_mixed_splits():
     """Mixed batch with a chunk at a 40k context and decodes up to 70k keys."""
     say("long-context mixed splits")
     b = wl.ragged_batch("lcm", [300, 1, 1, 1], [40300, 9001, 101, 70001], 32, 8, 128, 16, 7500, 81)
-    _sampled(b, 160, "long-context mixed")
+    _sampled(b, 160, "long-context mixed", typical=(8e-3, 1e-4))
 
 
 @pytest.mark.parametrize("n_seqs", [160, 161, 300])
@@ -287,3 +287,47 @@ def test_many_decode_sequences_order_and_scan(n_seqs):
     q[0], kv[0] = 40, 640   # one prefill chunk makes it a mixed batch
     b2 = wl.ragged_batch("many_mixed", q, kv, 8, 2, 128, 16, pool, 72, max_pages=48)
     _sampled(b2, 300, f"{n_seqs} mixed")
+
+
+@pytest.mark.parametrize("nsplit_ctx", [0, 6000])
+def test_uniform_prefill_batch_rank_by_rank(nsplit_ctx):
+    """Prefill-only batches whose sequences share q_len and kv_len run q-tile rank by rank
+    across the sequences; with and without KV splits (a long shared context), group size 4,
+    fused write, every output element against the oracle."""
+    say(f"uniform prefill batch, context {nsplit_ctx}")
+    q = [96, 96, 96]
+    kv = [96 + nsplit_ctx] * 3
+    pool = sum((k + 15) // 16 for k in kv) + 4
+    b = wl.ragged_batch("uni", q, kv, 8, 2, 64, 16, pool, 83 + nsplit_ctx)
+    d = Dev(b)
+    assert rpa.select_kernel(d.q, d.k_cache, d.tables, d.cu_h, d.kvl_h) == rpa.KERNEL_PREFILL
+    del d
+    _full_check(b, label=f"uniform prefill context {nsplit_ctx}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_bad_table_entry_is_never_stored_through(kernel):
+    """A block-table entry outside [0, num_pages) where only new tokens land (the precondition
+    broken): the fused write skips those stores, every other cache byte is as the oracle
+    writes it, and the outputs are exact (readers take new keys from k_new, never from the
+    cache).  rpa_write_kv skips them the same way."""
+    say(f"bad table entry kernel={kernel}")
+    b = wl.ragged_batch("bad", [1, 3, 20], [40, 35, 80], 8, 2, 128, 16, 20, 95)
+    page = int(b.block_tables[1, 2])          # sequence 1: past 32, new tokens in block 2
+    kc, vc = oracle_after_write(b)
+    ref = oracle.attention(b.q, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale, 16, 2)
+    kc_want, vc_want = kc.copy(), vc.copy()
+    kc_want[page], vc_want[page] = b.k_cache[page], b.v_cache[page]   # never written
+    for bad in (b.num_pages + 7, -1):
+        bb = wl.RaggedBatch(**{**b.__dict__})
+        bb.block_tables = b.block_tables.copy()
+        bb.block_tables[1, 2] = bad
+        d = Dev(bb)
+        out = d.attention(kernel=kernel)
+        assert np.array_equal(to_host_bits(d.k_cache), kc_want), f"entry {bad}: K cache differs"
+        assert np.array_equal(to_host_bits(d.v_cache), vc_want), f"entry {bad}: V cache differs"
+        compare(to_host_f32(out), ref, f"bad entry {bad} kernel={kernel}")
+        w = Dev(bb)
+        w.write()
+        assert np.array_equal(to_host_bits(w.k_cache), kc_want), f"entry {bad}: rpa_write_kv K"
+        assert np.array_equal(to_host_bits(w.v_cache), vc_want), f"entry {bad}: rpa_write_kv V"
