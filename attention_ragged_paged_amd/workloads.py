@@ -14,10 +14,11 @@ Draw order for every batch, from ``numpy.random.default_rng(seed)``:
   5. the block mask, for the block-sparse workload.
 
 FP8 caches (``kv_dtype="fp8"``) hold E4M3 codes (``uint8``) drawn directly, not
-quantized from values: sign uniform, exponent field ~ round(N(9, 0.8)) clipped
-to [1, 10], mantissa uniform, with the cache scales ``FP8_SCALE`` = 1/4, so cached
-values are of order one and below 4 in magnitude, like the N(0, 1) bf16 caches.
-Poisoned slots of an FP8 cache hold the NaN code 0x7F.
+quantized from values, with the cache scales ``FP8_SCALE`` = 1/4: half of the codes
+field by field (sign uniform, exponent field ~ round(N(9, 0.8)) clipped to [1, 10],
+mantissa uniform: values of order one, below 4 in magnitude, like the N(0, 1) bf16
+caches), half uniformly over every finite code (zero, subnormals, up to +-448, i.e.
+values up to 112 in magnitude).  Poisoned slots of an FP8 cache hold the NaN code 0x7F.
 
 Named workloads (shapes of Llama-3-8B attention: 32 query heads, 8 KV heads,
 head dim 128) follow the five configurations the path is built for; see
@@ -60,7 +61,9 @@ def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.nd
 
 
 def _fp8_codes(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
-    """E4M3 codes drawn field by field (see the module docstring), in chunks."""
+    """E4M3 codes (see the module docstring), in chunks: each code is, with probability 1/2,
+    drawn field by field around values of order one, else uniformly over all 254 finite codes
+    (zero, subnormals and +-448 included)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
     for s in range(0, n, chunk):
@@ -69,7 +72,10 @@ def _fp8_codes(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndar
         sign = rng.integers(0, 2, size=m, dtype=np.uint8)
         expo = np.clip(np.rint(rng.normal(9.0, 0.8, size=m)), 1, 10).astype(np.uint8)
         mant = rng.integers(0, 8, size=m, dtype=np.uint8)
-        out[s:e] = (sign << 7) | (expo << 3) | mant
+        typical = (sign << 7) | (expo << 3) | mant
+        anycode = rng.integers(0, 254, size=m, dtype=np.uint8)
+        anycode = np.where(anycode >= 0x7F, anycode + 1, anycode).astype(np.uint8)  # skip 0x7F
+        out[s:e] = np.where(rng.random(m) < 0.5, typical, anycode)
     return out.reshape(shape)
 
 

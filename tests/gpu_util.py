@@ -116,11 +116,57 @@ def sample_rows(b: wl.RaggedBatch, n, seed=0):
     return np.array(sorted(rows), np.int32)
 
 
-def compare(got_f32, want_f64, label):
+def compare(got_f32, want_f64, label, row_scale=None, typical=None):
+    """max-abs within ATOL, or, with row_scale ([rows] or [T, Hq], one value per output row),
+    within ATOL * max(1, row_scale) per row.  typical = (max_abs, mean_abs): bounds on the
+    error level itself, far below the contract, that catch regressions the contract would
+    let through."""
     err = np.abs(got_f32.astype(np.float64) - want_f64)
     finite = np.isfinite(got_f32).all()
     mx = float(err.max()) if err.size else 0.0
-    say(f"  {label}: max-abs {mx:.3e} mean-abs {float(err.mean()) if err.size else 0:.3e}")
-    assert finite, f"{label}: non-finite output"
-    assert mx <= ATOL, f"{label}: max-abs {mx} > {ATOL}"
+    mean = float(err.mean()) if err.size else 0.0
+    if row_scale is None:
+        say(f"  {label}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+        assert finite, f"{label}: non-finite output"
+        assert mx <= ATOL, f"{label}: max-abs {mx} > {ATOL}"
+    else:
+        tol = ATOL * np.maximum(1.0, np.asarray(row_scale, np.float64))[..., None]
+        rel = float((err / tol).max()) if err.size else 0.0
+        say(f"  {label}: max-abs {mx:.3e} mean-abs {mean:.3e}, worst error / row bound {rel:.3f}"
+            f" (largest row bound {float(tol.max()):.3g})")
+        assert finite, f"{label}: non-finite output"
+        assert rel <= 1.0, f"{label}: error {rel:.3f} x the row bound ATOL * max(1, max|V|)"
+    if typical is not None:
+        assert mx <= typical[0], f"{label}: max-abs {mx:.3e} above its usual level {typical[0]:.1e}"
+        assert mean <= typical[1], f"{label}: mean-abs {mean:.3e} above its usual level {typical[1]:.1e}"
     return mx
+
+
+def visible_vmax(b: wl.RaggedBatch, v_cache, rows=None):
+    """Largest |V| value (code value times v_scale for an FP8 cache) over the keys each output
+    row sees: [T, Hq], or [n] for sampled rows (token, head).  The bound of an FP8 row scales
+    with it: the bf16 rounding of probabilities and output is relative to the values."""
+    if v_cache.dtype == np.uint8:
+        lut = np.abs(oracle.fp8_decode(np.arange(256, dtype=np.uint8))) * b.v_scale
+        lut[np.isnan(lut)] = 0.0
+    else:
+        lut = None
+    S, Hkv, G = b.page_size, b.num_kv_heads, b.num_q_heads // b.num_kv_heads
+    out = np.zeros((b.total_q, b.num_q_heads))
+    for bi in range(b.num_seqs):
+        q0, q1 = int(b.cu_q_lens[bi]), int(b.cu_q_lens[bi + 1])
+        if q1 == q0:
+            continue
+        for g in range(Hkv):
+            L = int(b.kv_lens[bi] if b.layout == wl.SEQ_MAJOR else b.kv_lens[bi, g])
+            row = b.block_tables[bi] if b.layout == wl.SEQ_MAJOR else b.block_tables[bi, g]
+            j = np.arange(L)
+            idx = (row[j // S], j % S, np.full(L, g)) if b.layout == wl.SEQ_MAJOR else (row[j // S], j % S)
+            v = v_cache[idx]
+            m = lut[v].max(axis=1) if lut is not None else np.abs(wl.bf16_to_f32(v)).max(axis=1)
+            cm = np.maximum.accumulate(m)
+            past = L - (q1 - q0)
+            out[q0:q1, g * G:(g + 1) * G] = cm[past + np.arange(q1 - q0)][:, None]
+    if rows is not None:
+        return out[rows[:, 0], rows[:, 1]]
+    return out

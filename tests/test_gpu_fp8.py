@@ -1,11 +1,12 @@
 """GPU parity of the FP8 (E4M3) KV cache against the CPU oracle.
 
 Cache writes bit-exact: every stored code equals the oracle's encode of float32(x) * float32(1 /
-scale) (clamped to +-448, nearest even).  Attention over the codes within max-abs 2e-2 of the
-oracle, the bound of the bf16 path: both sides read the same dequantized values (every E4M3
-value is exact in bf16), so what remains is the bf16 rounding of probabilities and outputs,
-which grows with the values' magnitude; the cached values here stay below 4 in magnitude, as
-N(0, 1) bf16 values do (the generator's FP8 codes with scales near 1/4).
+scale) (clamped to +-448, nearest even).  Attention over the codes: both sides read the same
+dequantized values (every E4M3 value is exact in bf16), so what remains is the bf16 rounding of
+probabilities and outputs, which is relative to the values: each output row must lie within
+2e-2 * max(1, max |V| over the keys the row sees) of the oracle.  The caches hold codes over the
+whole E4M3 range (zero, subnormals, up to +-448: values up to 112 at the scale 1/4) beside
+codes of order one.
 """
 import numpy as np
 import pytest
@@ -15,7 +16,7 @@ import attention_ragged_paged_amd as rpa
 import oracle
 from attention_ragged_paged_amd import workloads as wl
 from tests.gpu_util import (Dev, bf16_dev, cache_host, compare, i32_dev, oracle_after_write,
-                            oracle_attention, sample_rows, say, to_host_f32)
+                            oracle_attention, sample_rows, say, to_host_f32, visible_vmax)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +43,7 @@ def _check(b, kernel=rpa.KERNEL_AUTO, fused=True, label=""):
     assert np.array_equal(cache_host(d.k_cache), kc), f"{label}: K cache differs"
     assert np.array_equal(cache_host(d.v_cache), vc), f"{label}: V cache differs"
     ref = oracle_attention(b, kc, vc)
-    return compare(to_host_f32(out), ref, label)
+    return compare(to_host_f32(out), ref, label, row_scale=visible_vmax(b, vc))
 
 
 @pytest.mark.parametrize("layout", [wl.SEQ_MAJOR, wl.HEAD_MAJOR])
@@ -113,7 +114,7 @@ def test_fp8_ragged_cases(qs, past, Hq, Hkv, S, D):
 def test_fp8_odd_scales_attention():
     say("fp8 attention with odd scales")
     b = _batch([1, 20, 1], [300, 80, 45], Hq=8, Hkv=2, seed=77)
-    b.k_scale, b.v_scale = 0.2113, 0.2671   # not powers of two; values still below 4
+    b.k_scale, b.v_scale = 0.2113, 0.2671   # not powers of two
     _check(b, label="fp8 odd scales")
 
 
@@ -142,7 +143,7 @@ def _sampled(b, n_rows, label):
     rows = sample_rows(b, n_rows)
     ref = oracle_attention(b, kc, vc, rows=rows)
     got = to_host_f32(out)[rows[:, 0], rows[:, 1]]
-    return compare(got, ref, label)
+    return compare(got, ref, label, row_scale=visible_vmax(b, vc, rows))
 
 
 def test_fp8_llama3_decode_full_size():
@@ -171,7 +172,7 @@ def test_fp8_graph_attention():
     assert np.array_equal(cache_host(d.k_cache), kc)
     assert np.array_equal(cache_host(d.v_cache), vc)
     ref = oracle_attention(b, kc, vc)
-    compare(to_host_f32(out), ref, "fp8 graph eager")
+    compare(to_host_f32(out), ref, "fp8 graph eager", row_scale=visible_vmax(b, vc))
     graph = torch.cuda.CUDAGraph()
     d.k_cache.copy_(k0)
     d.v_cache.copy_(v0)

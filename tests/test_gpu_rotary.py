@@ -11,7 +11,7 @@ import attention_ragged_paged_amd as rpa
 import oracle
 from attention_ragged_paged_amd import workloads as wl
 from tests.gpu_util import (Dev, bf16_dev, cache_host, compare, oracle_attention, say,
-                            to_host_bits, to_host_f32)
+                            to_host_bits, to_host_f32, visible_vmax)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,8 @@ def test_rotary_then_attention(kv_dtype):
     torch.cuda.synchronize()
     ref = oracle.attention(qo, kc, vc, b.block_tables, b.cu_q_lens, b.kv_lens, b.scale,
                            b.page_size, b.num_kv_heads, k_scale=b.k_scale, v_scale=b.v_scale)
-    compare(to_host_f32(out), ref, f"rotary + attention {kv_dtype}")
+    compare(to_host_f32(out), ref, f"rotary + attention {kv_dtype}",
+            row_scale=visible_vmax(b, vc) if kv_dtype == "fp8" else None)
 
 
 def test_rotary_llama3_prefill_size():
