@@ -909,7 +909,11 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
   const int v_rd_hi = (lds_off<D>(tr_key + 8, tr_c0) + 4 * (i16 & 1)) * 2;
 
   // One 64-key tile from LDS buffer tile & 1: S^T, (mask), online softmax, O^T += V^T P^T.
-  auto compute_tile = [&](int tile, auto par, auto masked) {
+  // mid() runs once the score MFMAs are issued: the next tile's loads go out while those
+  // MFMAs execute instead of before them, when every wave of the compute unit issues its
+  // loads at once after the barrier (measured: prefill 2.5% and block-union sparse 1.5%
+  // faster; interleaving the loads one by one between the MFMAs measured 2-9% slower).
+  auto compute_tile = [&](int tile, auto par, auto masked, auto mid) {
     const int kt0 = k_begin + tile * kPrefillKeys;
     const uint16_t *kt = kbuf[decltype(par)::value];
     const uint16_t *vt = vbuf[decltype(par)::value];
@@ -941,6 +945,7 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    mid();
     __builtin_amdgcn_s_setprio(0);
     // Row max on the raw scores: the scale is positive, so it is applied once to the max and
     // folded into the exponent below as one FMA per score.
@@ -1017,8 +1022,8 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       }
     }
   };
-  // Tile i: (writer: store its new keys), issue tile i+1 into the other buffer, compute
-  // tile i, wait for tile i+1 and meet at the barrier.  The buffer tile i+1 goes to was last
+  // Tile i: (writer: store its new keys), compute tile i, issuing tile i+1 into the other
+  // buffer once its score MFMAs are out, wait for tile i+1 and meet at the barrier.  The buffer tile i+1 goes to was last
   // read while computing tile i-1, which every wave finished before the previous barrier.
   // Buffers are chosen at compile time (tiles are taken in pairs), which keeps the two
   // buffers' accesses apart for the compiler.
@@ -1029,13 +1034,14 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
       // they are converted into the other buffer.
       const bool more = tile + 1 < n_tiles;
       if (more) load8(tile + 1);
-      compute_tile(tile, par, masked);
+      compute_tile(tile, par, masked, [] {});
       if (more) commit8(tile + 1, std::integral_constant<int, 1 - P>{});
       __syncthreads();
     } else {
       if (writer) write_new_rows(tile, par);
-      if (tile + 1 < n_tiles) issue_tile(tile + 1, std::integral_constant<int, 1 - P>{});
-      compute_tile(tile, par, masked);
+      compute_tile(tile, par, masked, [&] {
+        if (tile + 1 < n_tiles) issue_tile(tile + 1, std::integral_constant<int, 1 - P>{});
+      });
       wait_all_memory();
       __syncthreads();
     }

@@ -149,8 +149,8 @@ rpa_status validate(const rpa_shape *s, bool need_lens) {
   if (s->num_q_heads / s->num_kv_heads > rpa::kPrefillRows)
     return fail(RPA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per KV head",
                 s->num_q_heads / s->num_kv_heads, rpa::kPrefillRows);
-  if (!is_pow2(s->page_size) || s->page_size < 16)
-    return fail(RPA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two >= 16",
+  if (!is_pow2(s->page_size) || s->page_size < 16 || s->page_size > 1024)
+    return fail(RPA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two in [16, 1024]",
                 s->page_size);
   if (s->num_pages <= 0) return fail(RPA_ERR_INVALID_ARGUMENT, "num_pages %d <= 0", s->num_pages);
   if (s->max_pages_per_seq <= 0)

@@ -90,7 +90,8 @@ typedef struct rpa_shape {
   int32_t num_q_heads;        /* Hq, a multiple of Hkv */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* D: 64 or 128 */
-  int32_t page_size;          /* S: a power of two >= 16 (the PR's block_size rule) */
+  int32_t page_size;          /* S: a power of two in [16, 1024] (the PR's block_size rule,
+                                 capped at the largest size the kernels are tested on) */
   int32_t num_pages;          /* P: pages in each cache */
   int32_t max_pages_per_seq;  /* row length of the block table */
   int32_t layout;             /* RPA_LAYOUT_* */

@@ -77,6 +77,7 @@ def _attn(lib, s, scale=0.125, k_new=None, ws=None, ws_bytes=0, ptr=16):
     (dict(cu=[0, 1], kv=[4], Hq=3, Hkv=2), "not a multiple"),
     (dict(cu=[0, 1], kv=[4], S=24), "power of two"),
     (dict(cu=[0, 1], kv=[4], S=8), "power of two"),
+    (dict(cu=[0, 1], kv=[4], S=2048), "[16, 1024]"),
     (dict(cu=[0, 1], kv=[4], layout=5), "layout"),
     (dict(cu=[0, 1], kv=[4], kernel=9), "kernel"),
     (dict(cu=[0, 1], kv=[4], kv_dtype=3), "kv_dtype"),
