@@ -348,9 +348,31 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
   auto new_off = [&](int key) {
     return ((int64_t)(q0 + min(key, kv_len - 1) - past) * a.Hkv + g) * D + 16 * lchk;
   };
+  // A chunk's cache rows: a wave-uniform base (the chunk's first row, scalar arithmetic) plus
+  // a per-lane constant for load instruction t (row lrow + RPI t, the lane's 16 bytes).
+  constexpr int NL = KV8 ? NI8 : KK;
+  int lane_off[NL];
+#pragma unroll
+  for (int t = 0; t < NL; ++t)
+    lane_off[t] = (lrow + (KV8 ? RPI8 : RPI) * t) * (int)a.slot_stride + (KV8 ? 16 : 8) * lchk;
+  // Only a chunk whose last key reaches `past` holds new keys (wave-uniform): every other
+  // chunk takes a plain path, with no per-lane choice between cache and new rows.
+  auto has_new = [&](int key0) { return fused && key0 + 15 >= past; };
   auto load_chunk = [&](int base, int i, u32x4 *kr, u32x4 *vr) {
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
     const int page = read_page(__builtin_amdgcn_readlane(pg_lane, i));
+    if (!has_new(key0)) {
+      const int64_t cb = kv_row_offset(a, page, key0 & page_mask, g);
+      const uint8_t *const kb8 = reinterpret_cast<const uint8_t *>(a.k_cache + (KV8 ? 0 : cb)) + (KV8 ? cb : 0);
+      const uint8_t *const vb8 = reinterpret_cast<const uint8_t *>(a.v_cache + (KV8 ? 0 : cb)) + (KV8 ? cb : 0);
+      constexpr int EB = KV8 ? 1 : 2;  // bytes per cache element
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        kr[t] = *reinterpret_cast<const u32x4 *>(kb8 + EB * lane_off[t]);
+        vr[t] = *reinterpret_cast<const u32x4 *>(vb8 + EB * lane_off[t]);
+      }
+      return;
+    }
     if constexpr (KV8) {
       // register t: the row's 16 codes, or for a new key the first 8 of its bf16 values (the
       // other 8 are loaded when the chunk is staged); every lane loads, so the waits before
@@ -392,9 +414,25 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
     const int page = __builtin_amdgcn_readlane(pg_lane, i);  // negative: a bad entry, no store
     // Stage in LDS (V rows of keys past the item's range are zeroed: they may hold anything);
     // the writer item also stores the new keys into their page slots.
+    const bool fresh = has_new(key0);
     if constexpr (KV8) {
       // New keys are quantized here exactly as the cache stores them, so every reader sees
       // the stored codes; LDS holds the codes' bf16 values in the bf16 layout.
+      if (!fresh) {
+#pragma unroll
+        for (int t = 0; t < NI8; ++t) {
+          const int r = lrow + RPI8 * t;
+          u32x4 vc = vr[t];
+          if (key0 + r >= k_end) vc = u32x4{0u, 0u, 0u, 0u};
+          u32x4 lo, hi;
+          dequant16(kr[t], lo, hi);
+          *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, 2 * lchk)) = lo;
+          *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, 2 * lchk + 1)) = hi;
+          dequant16(vc, lo, hi);
+          *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk)) = lo;
+          *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk + 1)) = hi;
+        }
+      } else {
 #pragma unroll
       for (int t = 0; t < NI8; ++t) {
         const int r = lrow + RPI8 * t;
@@ -420,6 +458,7 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
         *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk)) = lo;
         *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, 2 * lchk + 1)) = hi;
       }
+      }
     } else {
 #pragma unroll
     for (int t = 0; t < KK; ++t) {
@@ -427,10 +466,17 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
       const int key = key0 + r;
       *reinterpret_cast<u32x4 *>(kbuf + lds_off<D>(r, lchk)) = kr[t];
       *reinterpret_cast<u32x4 *>(vbuf + lds_off<D>(r, lchk)) = key < k_end ? vr[t] : u32x4{0u, 0u, 0u, 0u};
-      if (writer && key >= past && key < k_end && page >= 0) {
-        const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 8 * lchk;
-        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + coff) = kr[t];
-        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + coff) = vr[t];
+    }
+    if (fresh && writer) {
+#pragma unroll
+      for (int t = 0; t < KK; ++t) {
+        const int r = lrow + RPI * t;
+        const int key = key0 + r;
+        if (key >= past && key < k_end && page >= 0) {
+          const int64_t coff = kv_row_offset(a, page, (key0 & page_mask) + r, g) + 8 * lchk;
+          *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_cache) + coff) = kr[t];
+          *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_cache) + coff) = vr[t];
+        }
       }
     }
     }
