@@ -362,10 +362,10 @@ __device__ void decode_item(const AttnArgs &a, int id, char *smem_raw, const Seq
     const int key0 = k_begin + 16 * (w + 4 * (base + i));
     const int page = read_page(__builtin_amdgcn_readlane(pg_lane, i));
     if (!has_new(key0)) {
-      const int64_t cb = kv_row_offset(a, page, key0 & page_mask, g);
-      const uint8_t *const kb8 = reinterpret_cast<const uint8_t *>(a.k_cache + (KV8 ? 0 : cb)) + (KV8 ? cb : 0);
-      const uint8_t *const vb8 = reinterpret_cast<const uint8_t *>(a.v_cache + (KV8 ? 0 : cb)) + (KV8 ? cb : 0);
       constexpr int EB = KV8 ? 1 : 2;  // bytes per cache element
+      const int64_t cb = kv_row_offset(a, page, key0 & page_mask, g) * EB;  // chunk base, bytes
+      const uint8_t *const kb8 = reinterpret_cast<const uint8_t *>(a.k_cache) + cb;
+      const uint8_t *const vb8 = reinterpret_cast<const uint8_t *>(a.v_cache) + cb;
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
         kr[t] = *reinterpret_cast<const u32x4 *>(kb8 + EB * lane_off[t]);
@@ -1069,8 +1069,9 @@ __device__ void prefill_item(const AttnArgs &a, int id, char *lds0, char *lds1, 
     }
   };
   // Tile i: (writer: store its new keys), compute tile i, issuing tile i+1 into the other
-  // buffer once its score MFMAs are out, wait for tile i+1 and meet at the barrier.  The buffer tile i+1 goes to was last
-  // read while computing tile i-1, which every wave finished before the previous barrier.
+  // buffer once its score MFMAs are out, wait for tile i+1 and meet at the barrier.  The
+  // buffer tile i+1 goes to was last read while computing tile i-1, which every wave
+  // finished before the previous barrier.
   // Buffers are chosen at compile time (tiles are taken in pairs), which keeps the two
   // buffers' accesses apart for the compiler.
   auto step = [&](int tile, auto par, auto masked) {
